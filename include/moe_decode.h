@@ -1,0 +1,157 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) decode-time MoE layer.
+ *
+ * One call of moe_decode_forward computes one Mixture-of-Experts layer for a
+ * decode step of `batch` tokens on one GPU:
+ *
+ *   z      = x Wr^T (+ b)                                   router logits
+ *   S, w   = top-k of z, softmax or sigmoid weights,         selection
+ *            renormalised over the selected experts
+ *   out    = [x] + S2 (silu(S1 x) * (S3 x))                  shared expert
+ *              + sum_{j in S} w_j W2_j (silu(W1_j x) * (W3_j x))
+ *
+ * The pages this follows (the Kimi K3 decode article, spke.com/es and /ko
+ * ai/article/3589, Part 1 sections 1 "shapes per workload", 3 "MoE
+ * scheduling and overlap" and 4 "weight prefetch"; the Hungarian summary "A
+ * vLLM ugynoki kodolassal gyorsitotta a Kimi K3-at", section "Kevesebb
+ * kernel") name the parts of this layer -- router scores, routed experts
+ * behind tensor parallelism, a shared expert on its own stream, small-matrix
+ * kernels at batch 1-2 and split-K kernels above, and a weight stream that
+ * bounds small-batch decode -- but give no formulas; the formulas above are
+ * the plain gated-SwiGLU reading.
+ *
+ * Conventions for every function:
+ *  - All tensor pointers are DEVICE pointers, 16-byte aligned, row-major,
+ *    owned by the caller; the library never frees them.
+ *  - Every function returns a moe_status; no C++ exception crosses the ABI.
+ *    On failure moe_decode_last_error() returns a message for the calling
+ *    thread (valid until that thread's next call into the library).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *  - A plan is not thread-safe; distinct plans are independent.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,      /* bad argument: NULL, out of range, misaligned, aliasing   */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid layer the kernels do not cover; use another path   */
+    MOE_ERR_HIP = 3,          /* a HIP runtime call failed; message holds hipGetErrorString */
+    MOE_ERR_NOMEM = 4,        /* host or device allocation failed                          */
+    MOE_ERR_STATE = 5         /* call not valid in the plan's current state                */
+} moe_status;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+
+/* Kernel family for the gate/up projection.
+ *  SMALL_M: every expert is a full-K GEMV tile (lanes stream weight rows,
+ *           fp32 dot products); the form for batch 1-2.
+ *  SPLIT_K: experts with at least `mfma_min_tokens` tokens use split-K MFMA
+ *           tiles (fp32 partials, last-arriving tile applies SiLU*up), the
+ *           others GEMV tiles; the form for larger batches.
+ *  AUTO:    SMALL_M for batch <= 2, SPLIT_K otherwise.                      */
+typedef enum { MOE_VARIANT_AUTO = 0, MOE_VARIANT_SMALL_M = 1, MOE_VARIANT_SPLIT_K = 2 } moe_variant;
+
+typedef struct moe_decode_config {
+    int32_t hidden;          /* H: multiple of 64, 64..16384                          */
+    int32_t n_experts;       /* E: routed experts, 1..1024                            */
+    int32_t top_k;           /* k: 1..min(E, 16)                                      */
+    int32_t inter;           /* I: routed-expert intermediate size, multiple of 64    */
+    int32_t shared_inter;    /* Is: 0 (no shared expert) or a multiple of I           */
+    int32_t batch;           /* B: tokens per forward, 1..64 (one plan per batch)     */
+    int32_t score_fn;        /* moe_score_fn                                          */
+    int32_t renormalize;     /* 1: selected weights divided by their sum              */
+    float routed_scale;      /* multiplies every routed weight (1.0 = none)           */
+    int32_t add_residual;    /* 1: out = x + ...; 0: out = layer output only          */
+    const float* router_bias;/* device fp32 [E] added to the logits, or NULL          */
+    int32_t force_variant;   /* moe_variant                                           */
+    int32_t mfma_min_tokens; /* SPLIT_K: token count from which an expert uses MFMA
+                                tiles; 0 = library default                           */
+} moe_decode_config;
+
+typedef struct moe_decode_plan_s* moe_decode_plan_t;
+
+typedef struct moe_decode_info {
+    int32_t variant;          /* resolved moe_variant (never AUTO)                       */
+    int32_t n_kernels;        /* kernel launches per forward                            */
+    int32_t mfma_min_tokens;  /* resolved threshold (SPLIT_K), else 0                   */
+    int32_t shared_mfma;      /* 1 if the shared expert runs on MFMA tiles              */
+    size_t workspace_bytes;   /* device workspace owned by the plan                     */
+} moe_decode_info;
+
+/* Per-step counters the kernels write on the device (read back for tests). */
+typedef struct moe_decode_stats {
+    int32_t n_unique;         /* |U|: distinct routed experts selected in the step      */
+    int32_t gemv_tiles;       /* routed gate/up tiles on the GEMV path                  */
+    int32_t mfma_tiles;       /* routed gate/up tiles on the split-K MFMA path          */
+    int32_t error_flags;      /* 0 = no device-side error was detected                  */
+} moe_decode_stats;
+
+/* Validates `cfg` and builds a plan on the host.  Creates no device state, so
+ * it works (and its errors can be tested) without a GPU.  router_bias is only
+ * stored, not dereferenced.  *out_plan is set to NULL on failure. */
+moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_plan);
+
+/* Runs the layer asynchronously on `stream`.
+ *   x        bf16 [B][H]                     layer input (and residual)
+ *   router_w bf16 [E][H]                     router weight, one row per expert
+ *   expert_w bf16 [E][2I][H] then [E][H][I]  per expert: W13 (rows 0..I-1 gate
+ *                                            W1, rows I..2I-1 up W3), then all
+ *                                            experts' down projections W2
+ *   shared_w bf16 [2Is][H] then [H][Is]      shared S13 (gate rows, up rows), S2;
+ *                                            ignored (may be NULL) when Is == 0
+ *   out      bf16 [B][H]                     result, round-to-nearest-even;
+ *                                            must not overlap x
+ * The first call on a device allocates the plan's workspace, a second stream
+ * and events, and records the launches into a HIP graph; later calls replay
+ * the graph, updating kernel arguments when the pointers change.  Work is
+ * enqueued on `stream` and the plan's private stream only; the call returns
+ * once it is enqueued.  Calls on one plan must not overlap (they share the
+ * workspace). */
+moe_status moe_decode_forward(moe_decode_plan_t plan, const void* x, const void* router_w,
+                              const void* expert_w, const void* shared_w, void* out,
+                              void* stream);
+
+/* Enqueues on `stream` device-to-device copies of the last forward's routing:
+ * topk_idx int32 [B][k] (expert ids, descending logit, ties to the lower id),
+ * topk_w fp32 [B][k] (routing weights in the same order), n_unique int32 [1],
+ * logits fp32 [B][E] (router logits including the bias).  Any destination may
+ * be NULL.  MOE_ERR_STATE before the first forward. */
+moe_status moe_decode_routing(moe_decode_plan_t plan, int32_t* topk_idx, float* topk_w,
+                              int32_t* n_unique, float* logits, void* stream);
+
+/* Synchronises the plan's streams and copies the device-side counters of the
+ * last forward to *stats (host memory).  MOE_ERR_STATE before the first forward. */
+moe_status moe_decode_read_stats(moe_decode_plan_t plan, moe_decode_stats* stats);
+
+/* Resolved plan properties (host memory). */
+moe_status moe_decode_plan_info(moe_decode_plan_t plan, moe_decode_info* info);
+
+/* Kernel timing.  While enabled, forward launches eagerly (no graph) and
+ * records a HIP event pair around every kernel on the stream that kernel is
+ * launched on.  moe_decode_profile_read synchronises those streams and writes,
+ * per kernel slot, the summed milliseconds and the launch count over all
+ * forwards since profiling was enabled (arrays of `cap` entries, host memory),
+ * the slot names into `names` (may be NULL), and the slot count to *n.
+ * At most 4096 forwards are recorded per enable. */
+moe_status moe_decode_set_profiling(moe_decode_plan_t plan, int32_t enable);
+moe_status moe_decode_profile_read(moe_decode_plan_t plan, int32_t cap, double* total_ms,
+                                   int32_t* launches, const char** names, int32_t* n);
+
+/* Frees the plan and everything it owns (waits for its streams).  NULL is a no-op. */
+moe_status moe_decode_destroy(moe_decode_plan_t plan);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* moe_decode_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_DECODE_H */

@@ -1,0 +1,592 @@
+// moe_decode.cpp -- host side of the C ABI declared in include/moe_decode.h.
+//
+// A plan validates the layer shape, resolves the kernel family (small-matrix
+// GEMV at batch <= 2, split-K above: the shape choice the Kimi K3 decode
+// article describes in Part 1 section 1) and sizes the workspace; it touches
+// no device.  The first forward allocates the workspace, a second stream and
+// events, and builds a HIP graph with the router -> gate/up -> down chain and
+// the shared expert's gate/up as a parallel branch joined before the down
+// projection (article Part 1 section 3: shared expert on its own stream,
+// overlapped with routing; "What's next": per-step host work replayed as a
+// graph).  Later forwards replay the graph, patching kernel arguments when the
+// caller's pointers change.  The eager path launches the same kernels on the
+// caller's stream and the plan's second stream with fork/join events, and is
+// used for per-kernel timing.
+#include "../../include/moe_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "moe_args.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+#define HIP_TRY(call)                                                                         \
+    do {                                                                                      \
+        hipError_t e_ = (call);                                                               \
+        if (e_ != hipSuccess)                                                                 \
+            return fail(MOE_ERR_HIP, "%s failed: %s (%s:%d)", #call, hipGetErrorString(e_),   \
+                        __FILE__, __LINE__);                                                  \
+    } while (0)
+
+constexpr int kDefaultMfmaMin = 8;
+constexpr int kMaxProfiledForwards = 1024;
+
+enum Slot { S_ROUTER = 0, S_GATEUP = 1, S_SHARED = 2, S_DOWN = 3, S_COUNT = 4 };
+const char* kSlotNames[S_COUNT] = {"router_topk", "gateup_routed", "gateup_shared", "down_combine"};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+    size_t meta, z, topk_idx, topk_w, act_e, act_off, perm, sh_act_e, sh_act_off, sh_perm;
+    size_t h, hs, g_acc, g_acc_s, tile_cnt, tile_cnt_s, total;
+};
+
+}  // namespace
+
+struct moe_decode_plan_s {
+    moe_decode_config cfg;
+    int variant;
+    int mfma_min;         // routed experts with >= this many tokens use MFMA tiles; 0 = never
+    int routed_gemv_tb;   // largest token count of a routed GEMV tile
+    bool shared_mfma;
+    int max_act;          // min(E, B*k)
+    int ksplit, kslice;
+    Layout L;
+
+    // device state (first forward)
+    bool ready = false;
+    int device = -1;
+    char* ws = nullptr;
+    hipStream_t s2 = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+
+    // argument blocks; the pointer fields are refreshed per forward
+    RouterArgs ra{};
+    GateUpArgs ga{}, gs{};
+    DownArgs da{};
+    KernelPick kr{}, kg{}, ks{}, kd{};
+
+    // graph
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipGraphNode_t n_router = nullptr, n_gateup = nullptr, n_shared = nullptr, n_down = nullptr;
+    const void* baked[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    bool have_forward = false;
+
+    // profiling
+    bool profiling = false;
+    std::vector<hipEvent_t> prof_events;  // [forward][slot][start,end]
+    int prof_count = 0;
+};
+
+namespace {
+
+bool has_shared(const moe_decode_plan_s* p) { return p->cfg.shared_inter > 0; }
+
+moe_status validate(const moe_decode_config* c) {
+    if (!c) return fail(MOE_ERR_INVALID, "config is NULL");
+    if (c->hidden < 1 || c->n_experts < 1 || c->top_k < 1 || c->inter < 1 || c->batch < 1 ||
+        c->shared_inter < 0)
+        return fail(MOE_ERR_INVALID, "sizes must be positive (hidden %d, experts %d, top_k %d, "
+                    "inter %d, batch %d, shared_inter %d)", c->hidden, c->n_experts, c->top_k,
+                    c->inter, c->batch, c->shared_inter);
+    if (c->top_k > c->n_experts)
+        return fail(MOE_ERR_INVALID, "top_k %d exceeds n_experts %d", c->top_k, c->n_experts);
+    if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID)
+        return fail(MOE_ERR_INVALID, "score_fn %d is not a moe_score_fn", c->score_fn);
+    if ((c->renormalize != 0 && c->renormalize != 1) || (c->add_residual != 0 && c->add_residual != 1))
+        return fail(MOE_ERR_INVALID, "renormalize and add_residual must be 0 or 1");
+    if (!std::isfinite(c->routed_scale))
+        return fail(MOE_ERR_INVALID, "routed_scale must be finite");
+    if (c->force_variant < MOE_VARIANT_AUTO || c->force_variant > MOE_VARIANT_SPLIT_K)
+        return fail(MOE_ERR_INVALID, "force_variant %d is not a moe_variant", c->force_variant);
+    if (c->mfma_min_tokens < 0)
+        return fail(MOE_ERR_INVALID, "mfma_min_tokens must be >= 0");
+    if (c->router_bias && (reinterpret_cast<uintptr_t>(c->router_bias) & 3))
+        return fail(MOE_ERR_INVALID, "router_bias must be 4-byte aligned");
+    // shapes the kernels cover
+    if (c->hidden % 64 || c->hidden > 16384)
+        return fail(MOE_ERR_UNSUPPORTED, "hidden %d: need a multiple of 64 up to 16384", c->hidden);
+    if (c->n_experts > kMaxExperts)
+        return fail(MOE_ERR_UNSUPPORTED, "n_experts %d > %d", c->n_experts, kMaxExperts);
+    if (c->top_k > kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k %d > %d", c->top_k, kMaxTopK);
+    if (c->batch > kMaxBatch) return fail(MOE_ERR_UNSUPPORTED, "batch %d > %d", c->batch, kMaxBatch);
+    const int I = c->inter;
+    const bool i_ok = (I == 64 || I == 128 || I == 256) || (I % 512 == 0 && I <= 4096);
+    if (!i_ok)
+        return fail(MOE_ERR_UNSUPPORTED, "inter %d: need 64, 128, 256 or a multiple of 512 up to 4096", I);
+    if (c->shared_inter && (c->shared_inter % I || c->shared_inter > 8 * 4096))
+        return fail(MOE_ERR_UNSUPPORTED, "shared_inter %d: need 0 or a multiple of inter %d", c->shared_inter, I);
+    return MOE_OK;
+}
+
+Layout make_layout(const moe_decode_config& c, int max_act, bool split) {
+    const size_t B = c.batch, E = c.n_experts, k = c.top_k, I = c.inter, Is = c.shared_inter;
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t r = o;
+        o = align_up(o + bytes, 256);
+        return r;
+    };
+    L.meta = take(M_COUNT * 4);
+    L.z = take(B * E * 4);
+    L.topk_idx = take(B * k * 4);
+    L.topk_w = take(B * k * 4);
+    L.act_e = take((size_t)max_act * 4);
+    L.act_off = take(((size_t)max_act + 1) * 4);
+    L.perm = take(B * k * 4);
+    L.sh_act_e = take(4);
+    L.sh_act_off = take(8);
+    L.sh_perm = take(B * 4);
+    L.h = take(B * k * I * 4);
+    L.hs = take(B * (Is ? Is : 1) * 4);
+    if (split) {
+        L.g_acc = take(B * k * 2 * I * 4);
+        L.g_acc_s = take(B * 2 * (Is ? Is : 1) * 4);
+        L.tile_cnt = take((size_t)max_act * (I / kPairsPerMfmaTile) * 4);
+        L.tile_cnt_s = take((Is / kPairsPerMfmaTile + 1) * 4);
+    }
+    L.total = o;
+    return L;
+}
+
+template <class T>
+T* at(moe_decode_plan_s* p, size_t off) {
+    return reinterpret_cast<T*>(p->ws + off);
+}
+
+// Fills the argument blocks whose pointers do not depend on the caller.
+void fill_static_args(moe_decode_plan_s* p) {
+    const moe_decode_config& c = p->cfg;
+    const bool split = p->variant == MOE_VARIANT_SPLIT_K;
+    RouterArgs& r = p->ra;
+    r.bias = c.router_bias;
+    r.z = at<float>(p, p->L.z);
+    r.topk_idx = at<int32_t>(p, p->L.topk_idx);
+    r.topk_w = at<float>(p, p->L.topk_w);
+    r.meta = at<int32_t>(p, p->L.meta);
+    r.act_e = at<int32_t>(p, p->L.act_e);
+    r.act_off = at<int32_t>(p, p->L.act_off);
+    r.perm = at<int32_t>(p, p->L.perm);
+    r.H = c.hidden;
+    r.E = c.n_experts;
+    r.k = c.top_k;
+    r.B = c.batch;
+    r.score_fn = c.score_fn;
+    r.renormalize = c.renormalize;
+    r.routed_scale = c.routed_scale;
+    r.mfma_min_tokens = p->mfma_min;
+    r.tiles_per_expert = c.inter / kPairsPerGemvTile;
+    r.mfma_tiles_per_expert = (c.inter / kPairsPerMfmaTile) * p->ksplit;
+
+    GateUpArgs& g = p->ga;
+    g.expert_stride = 2LL * c.inter * c.hidden;
+    g.n_act = at<int32_t>(p, p->L.meta) + M_NACT;
+    g.act_e = r.act_e;
+    g.act_off = r.act_off;
+    g.perm = r.perm;
+    g.pair_div = c.top_k;
+    g.h = at<float>(p, p->L.h);
+    g.g_acc = split ? at<float>(p, p->L.g_acc) : nullptr;
+    g.tile_cnt = split ? at<uint32_t>(p, p->L.tile_cnt) : nullptr;
+    g.meta = r.meta;
+    g.H = c.hidden;
+    g.n = c.inter;
+    g.tiles_per_expert = c.inter / kPairsPerGemvTile;
+    g.mfma_min_tokens = p->mfma_min;
+    g.ksplit = p->ksplit;
+    g.kslice = p->kslice;
+
+    if (has_shared(p)) {
+        GateUpArgs& s = p->gs;
+        s.expert_stride = 0;
+        s.n_act = at<int32_t>(p, p->L.meta) + M_SHARED_NACT;
+        s.act_e = at<int32_t>(p, p->L.sh_act_e);
+        s.act_off = at<int32_t>(p, p->L.sh_act_off);
+        s.perm = at<int32_t>(p, p->L.sh_perm);
+        s.pair_div = 1;
+        s.h = at<float>(p, p->L.hs);
+        s.g_acc = split ? at<float>(p, p->L.g_acc_s) : nullptr;
+        s.tile_cnt = split ? at<uint32_t>(p, p->L.tile_cnt_s) : nullptr;
+        s.meta = r.meta;
+        s.H = c.hidden;
+        s.n = c.shared_inter;
+        s.tiles_per_expert = c.shared_inter / kPairsPerGemvTile;
+        s.mfma_min_tokens = p->shared_mfma ? 1 : 0;
+        s.ksplit = p->ksplit;
+        s.kslice = p->kslice;
+    }
+
+    DownArgs& d = p->da;
+    d.n_act = g.n_act;
+    d.act_e = r.act_e;
+    d.act_off = r.act_off;
+    d.perm = r.perm;
+    d.topk_w = r.topk_w;
+    d.h = g.h;
+    d.hs = at<float>(p, p->L.hs);
+    d.H = c.hidden;
+    d.I = c.inter;
+    d.Is = c.shared_inter;
+    d.B = c.batch;
+    d.k = c.top_k;
+    d.add_residual = c.add_residual;
+}
+
+void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, const void* expert_w,
+                  const void* shared_w, void* out) {
+    const moe_decode_config& c = p->cfg;
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* ew = static_cast<const uint16_t*>(expert_w);
+    const uint16_t* sw = static_cast<const uint16_t*>(shared_w);
+    p->ra.x = xb;
+    p->ra.wr = static_cast<const uint16_t*>(router_w);
+    p->ga.x = xb;
+    p->ga.w = ew;
+    p->gs.x = xb;
+    p->gs.w = sw;
+    p->da.x = xb;
+    p->da.w2 = ew + (size_t)c.n_experts * 2 * c.inter * c.hidden;
+    p->da.s2 = has_shared(p) ? sw + (size_t)2 * c.shared_inter * c.hidden : nullptr;
+    p->da.out = static_cast<uint16_t*>(out);
+    p->kr = pick_router(p->ra);
+    p->kg = pick_gateup(p->ga, p->max_act, p->routed_gemv_tb);
+    if (has_shared(p)) p->ks = pick_gateup(p->gs, 1, c.batch);
+    p->kd = pick_down(p->da);
+}
+
+moe_status device_init(moe_decode_plan_s* p, hipStream_t stream) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (p->ready) {
+        if (dev != p->device)
+            return fail(MOE_ERR_STATE, "plan was set up on device %d, current device is %d", p->device, dev);
+        return MOE_OK;
+    }
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->ws), p->L.total);
+    if (e != hipSuccess) {
+        p->ws = nullptr;
+        return fail(MOE_ERR_NOMEM, "hipMalloc of %zu workspace bytes failed: %s", p->L.total,
+                    hipGetErrorString(e));
+    }
+    p->device = dev;
+    HIP_TRY(hipStreamCreateWithFlags(&p->s2, hipStreamNonBlocking));
+    HIP_TRY(hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming));
+    // zero once: counters re-arm themselves and split-K partials are cleared after use
+    HIP_TRY(hipMemsetAsync(p->ws, 0, p->L.total, stream));
+    fill_static_args(p);
+    InitArgs ia{at<int32_t>(p, p->L.meta), at<int32_t>(p, p->L.sh_act_e), at<int32_t>(p, p->L.sh_act_off),
+                at<int32_t>(p, p->L.sh_perm), p->cfg.batch};
+    KernelPick ki = pick_init(ia);
+    void* args[] = {&ia};
+    HIP_TRY(hipLaunchKernel(ki.func, ki.grid, ki.block, args, 0, stream));
+    p->ready = true;
+    return MOE_OK;
+}
+
+moe_status launch(const KernelPick& k, void* args, hipStream_t s) {
+    void* a[] = {args};
+    HIP_TRY(hipLaunchKernel(k.func, k.grid, k.block, a, 0, s));
+    return MOE_OK;
+}
+
+// Eager launch on the caller's stream and the plan's second stream.
+moe_status enqueue_eager(moe_decode_plan_s* p, hipStream_t stream, hipEvent_t* ev) {
+    moe_status st;
+    const bool sh = has_shared(p);
+    if (sh) {
+        HIP_TRY(hipEventRecord(p->ev_fork, stream));
+        HIP_TRY(hipStreamWaitEvent(p->s2, p->ev_fork, 0));
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_SHARED], p->s2));
+        if ((st = launch(p->ks, &p->gs, p->s2))) return st;
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_SHARED + 1], p->s2));
+        HIP_TRY(hipEventRecord(p->ev_join, p->s2));
+    }
+    if (ev) HIP_TRY(hipEventRecord(ev[2 * S_ROUTER], stream));
+    if ((st = launch(p->kr, &p->ra, stream))) return st;
+    if (ev) HIP_TRY(hipEventRecord(ev[2 * S_ROUTER + 1], stream));
+    if (ev) HIP_TRY(hipEventRecord(ev[2 * S_GATEUP], stream));
+    if ((st = launch(p->kg, &p->ga, stream))) return st;
+    if (ev) HIP_TRY(hipEventRecord(ev[2 * S_GATEUP + 1], stream));
+    if (sh) HIP_TRY(hipStreamWaitEvent(stream, p->ev_join, 0));
+    if (ev) HIP_TRY(hipEventRecord(ev[2 * S_DOWN], stream));
+    if ((st = launch(p->kd, &p->da, stream))) return st;
+    if (ev) HIP_TRY(hipEventRecord(ev[2 * S_DOWN + 1], stream));
+    return MOE_OK;
+}
+
+hipKernelNodeParams node_params(const KernelPick& k, void** args) {
+    hipKernelNodeParams np{};
+    np.blockDim = k.block;
+    np.gridDim = k.grid;
+    np.func = const_cast<void*>(k.func);
+    np.kernelParams = args;
+    np.sharedMemBytes = 0;
+    np.extra = nullptr;
+    return np;
+}
+
+moe_status build_graph(moe_decode_plan_s* p) {
+    HIP_TRY(hipGraphCreate(&p->graph, 0));
+    void* ar[] = {&p->ra};
+    void* ag[] = {&p->ga};
+    void* as[] = {&p->gs};
+    void* ad[] = {&p->da};
+    hipKernelNodeParams np = node_params(p->kr, ar);
+    HIP_TRY(hipGraphAddKernelNode(&p->n_router, p->graph, nullptr, 0, &np));
+    np = node_params(p->kg, ag);
+    HIP_TRY(hipGraphAddKernelNode(&p->n_gateup, p->graph, &p->n_router, 1, &np));
+    hipGraphNode_t deps[2] = {p->n_gateup, nullptr};
+    int ndeps = 1;
+    if (has_shared(p)) {
+        np = node_params(p->ks, as);
+        HIP_TRY(hipGraphAddKernelNode(&p->n_shared, p->graph, nullptr, 0, &np));
+        deps[ndeps++] = p->n_shared;
+    }
+    np = node_params(p->kd, ad);
+    HIP_TRY(hipGraphAddKernelNode(&p->n_down, p->graph, deps, ndeps, &np));
+    HIP_TRY(hipGraphInstantiate(&p->exec, p->graph, nullptr, nullptr, 0));
+    return MOE_OK;
+}
+
+moe_status patch_graph(moe_decode_plan_s* p) {
+    void* ar[] = {&p->ra};
+    void* ag[] = {&p->ga};
+    void* as[] = {&p->gs};
+    void* ad[] = {&p->da};
+    hipKernelNodeParams np = node_params(p->kr, ar);
+    HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_router, &np));
+    np = node_params(p->kg, ag);
+    HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_gateup, &np));
+    if (has_shared(p)) {
+        np = node_params(p->ks, as);
+        HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_shared, &np));
+    }
+    np = node_params(p->kd, ad);
+    HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_down, &np));
+    return MOE_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool misaligned(const void* p) { return reinterpret_cast<uintptr_t>(p) & 15; }
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_plan) {
+    g_err.clear();
+    if (!out_plan) return fail(MOE_ERR_INVALID, "out_plan is NULL");
+    *out_plan = nullptr;
+    moe_status st = validate(cfg);
+    if (st) return st;
+    moe_decode_plan_s* p = new (std::nothrow) moe_decode_plan_s();
+    if (!p) return fail(MOE_ERR_NOMEM, "host allocation of the plan failed");
+    p->cfg = *cfg;
+    const moe_decode_config& c = p->cfg;
+    p->variant = c.force_variant != MOE_VARIANT_AUTO ? c.force_variant
+                 : (c.batch <= 2 ? MOE_VARIANT_SMALL_M : MOE_VARIANT_SPLIT_K);
+    if (p->variant == MOE_VARIANT_SPLIT_K) {
+        p->mfma_min = c.mfma_min_tokens ? c.mfma_min_tokens : kDefaultMfmaMin;
+        if (p->mfma_min > kMaxBatch + 1) p->mfma_min = kMaxBatch + 1;
+        p->routed_gemv_tb = std::min(c.batch, p->mfma_min - 1);
+        if (p->routed_gemv_tb < 1) p->routed_gemv_tb = 1;
+        p->shared_mfma = c.batch >= p->mfma_min;
+    } else {
+        p->mfma_min = 0;
+        p->routed_gemv_tb = c.batch;
+        p->shared_mfma = false;
+    }
+    p->max_act = std::min(c.n_experts, c.batch * c.top_k);
+    // K split of an MFMA row block: the most splits <= 16 that divide H into multiples of 32
+    p->ksplit = 1;
+    for (int s = kSplitK; s >= 1; --s)
+        if (c.hidden % (32 * s) == 0) { p->ksplit = s; break; }
+    p->kslice = c.hidden / p->ksplit;
+    p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K);
+    *out_plan = p;
+    return MOE_OK;
+}
+
+moe_status moe_decode_forward(moe_decode_plan_t p, const void* x, const void* router_w,
+                              const void* expert_w, const void* shared_w, void* out, void* stream_) {
+    g_err.clear();
+    if (!p) return fail(MOE_ERR_INVALID, "plan is NULL");
+    const moe_decode_config& c = p->cfg;
+    if (!x || !router_w || !expert_w || !out || (c.shared_inter > 0 && !shared_w))
+        return fail(MOE_ERR_INVALID, "NULL tensor pointer");
+    if (misaligned(x) || misaligned(router_w) || misaligned(expert_w) || misaligned(out) ||
+        (c.shared_inter > 0 && misaligned(shared_w)))
+        return fail(MOE_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+    const size_t act_bytes = (size_t)c.batch * c.hidden * 2;
+    if (overlaps(x, act_bytes, out, act_bytes)) return fail(MOE_ERR_INVALID, "out overlaps x");
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    moe_status st = device_init(p, stream);
+    if (st) return st;
+    if (!has_shared(p)) shared_w = nullptr;
+    const void* tuple[5] = {x, router_w, expert_w, shared_w, out};
+    const bool changed = std::memcmp(tuple, p->baked, sizeof tuple) != 0;
+    if (changed || !p->have_forward) set_pointers(p, x, router_w, expert_w, shared_w, out);
+    p->have_forward = true;
+
+    if (p->profiling) {
+        if (p->prof_count >= kMaxProfiledForwards)
+            return fail(MOE_ERR_STATE, "profiling records at most %d forwards", kMaxProfiledForwards);
+        const size_t base = (size_t)p->prof_count * S_COUNT * 2;
+        while (p->prof_events.size() < base + S_COUNT * 2) {
+            hipEvent_t ev;
+            HIP_TRY(hipEventCreate(&ev));
+            p->prof_events.push_back(ev);
+        }
+        st = enqueue_eager(p, stream, &p->prof_events[base]);
+        if (st) return st;
+        ++p->prof_count;
+        std::memcpy(p->baked, tuple, sizeof tuple);
+        return MOE_OK;
+    }
+    if (!p->exec) {
+        st = build_graph(p);
+        if (st) return st;
+    } else if (changed) {
+        st = patch_graph(p);
+        if (st) return st;
+    }
+    std::memcpy(p->baked, tuple, sizeof tuple);
+    HIP_TRY(hipGraphLaunch(p->exec, stream));
+    return MOE_OK;
+}
+
+moe_status moe_decode_routing(moe_decode_plan_t p, int32_t* topk_idx, float* topk_w, int32_t* n_unique,
+                              float* logits, void* stream_) {
+    g_err.clear();
+    if (!p) return fail(MOE_ERR_INVALID, "plan is NULL");
+    if (!p->have_forward) return fail(MOE_ERR_STATE, "no forward has run on this plan");
+    hipStream_t s = static_cast<hipStream_t>(stream_);
+    const size_t n = (size_t)p->cfg.batch * p->cfg.top_k;
+    if (topk_idx) HIP_TRY(hipMemcpyAsync(topk_idx, p->ws + p->L.topk_idx, n * 4, hipMemcpyDeviceToDevice, s));
+    if (topk_w) HIP_TRY(hipMemcpyAsync(topk_w, p->ws + p->L.topk_w, n * 4, hipMemcpyDeviceToDevice, s));
+    if (n_unique)
+        HIP_TRY(hipMemcpyAsync(n_unique, p->ws + p->L.meta + 4 * M_NACT, 4, hipMemcpyDeviceToDevice, s));
+    if (logits)
+        HIP_TRY(hipMemcpyAsync(logits, p->ws + p->L.z, (size_t)p->cfg.batch * p->cfg.n_experts * 4,
+                               hipMemcpyDeviceToDevice, s));
+    return MOE_OK;
+}
+
+moe_status moe_decode_read_stats(moe_decode_plan_t p, moe_decode_stats* stats) {
+    g_err.clear();
+    if (!p || !stats) return fail(MOE_ERR_INVALID, "NULL argument");
+    if (!p->have_forward) return fail(MOE_ERR_STATE, "no forward has run on this plan");
+    HIP_TRY(hipDeviceSynchronize());
+    int32_t meta[M_COUNT];
+    HIP_TRY(hipMemcpy(meta, p->ws + p->L.meta, sizeof meta, hipMemcpyDeviceToHost));
+    stats->n_unique = meta[M_NACT];
+    stats->gemv_tiles = meta[M_GEMV_TILES];
+    stats->mfma_tiles = meta[M_MFMA_TILES];
+    stats->error_flags = meta[M_ERR];
+    return MOE_OK;
+}
+
+moe_status moe_decode_plan_info(moe_decode_plan_t p, moe_decode_info* info) {
+    g_err.clear();
+    if (!p || !info) return fail(MOE_ERR_INVALID, "NULL argument");
+    info->variant = p->variant;
+    info->n_kernels = 3 + (p->cfg.shared_inter > 0 ? 1 : 0);
+    info->mfma_min_tokens = p->mfma_min;
+    info->shared_mfma = p->shared_mfma ? 1 : 0;
+    info->workspace_bytes = p->L.total;
+    return MOE_OK;
+}
+
+moe_status moe_decode_set_profiling(moe_decode_plan_t p, int32_t enable) {
+    g_err.clear();
+    if (!p) return fail(MOE_ERR_INVALID, "plan is NULL");
+    if (p->ready) {
+        HIP_TRY(hipDeviceSynchronize());
+    }
+    for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
+    p->prof_events.clear();
+    p->prof_count = 0;
+    p->profiling = enable != 0;
+    return MOE_OK;
+}
+
+moe_status moe_decode_profile_read(moe_decode_plan_t p, int32_t cap, double* total_ms, int32_t* launches,
+                                   const char** names, int32_t* n) {
+    g_err.clear();
+    if (!p || !n || cap < 0 || (cap > 0 && (!total_ms || !launches)))
+        return fail(MOE_ERR_INVALID, "bad argument");
+    *n = S_COUNT;
+    for (int s = 0; s < S_COUNT && s < cap; ++s) {
+        total_ms[s] = 0.0;
+        launches[s] = 0;
+        if (names) names[s] = kSlotNames[s];
+    }
+    if (p->prof_count == 0) return MOE_OK;
+    for (int f = 0; f < p->prof_count; ++f) {
+        for (int s = 0; s < S_COUNT && s < cap; ++s) {
+            if (s == S_SHARED && !has_shared(p)) continue;
+            hipEvent_t a = p->prof_events[((size_t)f * S_COUNT + s) * 2];
+            hipEvent_t b = p->prof_events[((size_t)f * S_COUNT + s) * 2 + 1];
+            HIP_TRY(hipEventSynchronize(b));
+            float ms = 0.0f;
+            HIP_TRY(hipEventElapsedTime(&ms, a, b));
+            total_ms[s] += ms;
+            launches[s] += 1;
+        }
+    }
+    return MOE_OK;
+}
+
+moe_status moe_decode_destroy(moe_decode_plan_t p) {
+    g_err.clear();
+    if (!p) return MOE_OK;
+    moe_status st = MOE_OK;
+    if (p->ready) {
+        (void)hipSetDevice(p->device);
+        if (hipDeviceSynchronize() != hipSuccess) st = fail(MOE_ERR_HIP, "synchronize before destroy failed");
+        for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
+        if (p->exec) (void)hipGraphExecDestroy(p->exec);
+        if (p->graph) (void)hipGraphDestroy(p->graph);
+        if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
+        if (p->ev_join) (void)hipEventDestroy(p->ev_join);
+        if (p->s2) (void)hipStreamDestroy(p->s2);
+        if (p->ws) (void)hipFree(p->ws);
+    }
+    delete p;
+    return st;
+}
+
+const char* moe_decode_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,195 @@
+"""Parity of the HIP layer (through the C-ABI) against the fp64 CPU oracle.
+
+Workloads: the tiny shape (H 256, E 8, top-2 softmax, I = Is = 128), the
+TP8-shard shape (H 7168, E 384, top-8 sigmoid, I = Is = 256) with uniform,
+unit-logit and Zipf-skewed routing, and the unsharded shape (I = Is = 2048)
+on sampled tokens; plus edge shapes.  Comparison rules: tests/gpu_harness.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_29_amd as moe
+import oracle
+import synthetic
+from gpu_harness import DeviceLayer, compare, gap_x, make_plan, run_gpu, run_oracle, shape_of
+
+pytestmark = pytest.mark.gpu
+
+
+def check(layer, shape, batch, label, offset=0, sample=None, **plan_kw):
+    x, _ = gap_x(layer, shape, batch, offset)
+    plan = make_plan(layer, shape, batch, **plan_kw)
+    out, idx, w, nu = run_gpu(plan, layer, x, shape)
+    rows = np.arange(batch) if sample is None else np.asarray(sample)
+    out64, idx_o, w_o = run_oracle(layer, shape, x[rows])
+    m = compare(out[torch.from_numpy(rows).cuda()], idx[rows], w[rows], out64, idx_o, w_o, label)
+    if sample is None:
+        assert nu == len(np.unique(idx_o)), "n_unique"
+    st = plan.stats()
+    assert st.error_flags == 0
+    assert st.n_unique == nu
+    info = plan.info()
+    plan.destroy()
+    return m, st, info
+
+
+# ----------------------------------------------------------------- tiny shape
+
+@pytest.fixture(scope="module")
+def tiny():
+    return DeviceLayer(synthetic.TINY)
+
+
+@pytest.mark.parametrize("resid", [1, 0])
+@pytest.mark.parametrize("batch", [1, 2, 3, 8, 16, 33, 64])
+def test_tiny(tiny, batch, resid):
+    shape = shape_of(synthetic.TINY, add_residual=resid)
+    check(tiny, shape, batch, "tiny B=%d resid=%d" % (batch, resid))
+
+
+@pytest.mark.parametrize("batch,kw", [
+    (8, dict(force_variant=moe.VARIANT_SMALL_M)),
+    (64, dict(force_variant=moe.VARIANT_SMALL_M)),
+    (1, dict(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=1)),
+    (5, dict(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=1)),
+    (64, dict(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=2)),
+])
+def test_tiny_forced_variants(tiny, batch, kw):
+    shape = shape_of(synthetic.TINY, add_residual=0)
+    m, st, info = check(tiny, shape, batch, "tiny forced B=%d %s" % (batch, kw), **kw)
+    assert info.variant == kw["force_variant"]
+    if kw.get("mfma_min_tokens") == 1:
+        assert st.mfma_tiles > 0 and st.gemv_tiles == 0
+
+
+# ------------------------------------------------------------ TP8-shard shape
+
+@pytest.fixture(scope="module")
+def tp8():
+    return DeviceLayer(synthetic.TP8)
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 8, 16, 64])
+def test_tp8_uniform(tp8, batch):
+    shape = shape_of(synthetic.TP8)
+    m, st, info = check(tp8, shape, batch, "tp8 B=%d" % batch)
+    assert info.variant == (moe.VARIANT_SMALL_M if batch <= 2 else moe.VARIANT_SPLIT_K)
+
+
+def test_tp8_moe_only(tp8):
+    shape = shape_of(synthetic.TP8, add_residual=0)
+    check(tp8, shape, 16, "tp8 B=16 no residual")
+
+
+@pytest.fixture(scope="module")
+def tp8_unit():
+    return DeviceLayer(synthetic.TP8_UNIT)
+
+
+@pytest.mark.parametrize("batch", [8, 16])
+def test_tp8_unit_logits(tp8_unit, batch):
+    check(tp8_unit, shape_of(synthetic.TP8_UNIT), batch, "tp8 unit-logit B=%d" % batch)
+
+
+@pytest.fixture(scope="module")
+def tp8_zipf():
+    return DeviceLayer(synthetic.TP8_ZIPF)
+
+
+def test_tp8_zipf_skew(tp8_zipf):
+    m, st, info = check(tp8_zipf, shape_of(synthetic.TP8_ZIPF), 64, "tp8 zipf B=64")
+    assert st.mfma_tiles > 0, "hot experts should take the MFMA tiles"
+    assert st.n_unique < 200
+
+
+def test_tp8_identical_tokens_route_together(tp8):
+    """Every token identical: the k selected experts each get all B tokens, so
+    the routed experts go through the split-K MFMA tiles."""
+    shape = shape_of(synthetic.TP8)
+    B = 16
+    x1, _ = gap_x(tp8, shape, 1, offset=500)
+    x = np.repeat(x1, B, axis=0)
+    plan = make_plan(tp8, shape, B)
+    out, idx, w, nu = run_gpu(plan, tp8, x, shape)
+    out64, idx_o, w_o = run_oracle(tp8, shape, x)
+    compare(out, idx, w, out64, idx_o, w_o, "identical tokens")
+    st = plan.stats()
+    assert nu == 8 and st.mfma_tiles > 0 and st.gemv_tiles == 0
+    plan.destroy()
+
+
+def test_graph_replay_with_changing_inputs(tp8):
+    """One plan, many forwards with new x/out tensors and eager torch work in
+    between: every replay must match the oracle."""
+    shape = shape_of(synthetic.TP8)
+    B = 4
+    plan = make_plan(tp8, shape, B)
+    for it in range(4):
+        x, _ = gap_x(tp8, shape, B, offset=100 + 10 * it)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
+        out, idx, w, nu = run_gpu(plan, tp8, x, shape)
+        out64, idx_o, w_o = run_oracle(tp8, shape, x)
+        compare(out, idx, w, out64, idx_o, w_o, "replay %d" % it)
+        assert torch.isfinite(junk)
+    plan.destroy()
+
+
+def test_profiling_path_matches(tp8):
+    shape = shape_of(synthetic.TP8)
+    B = 16
+    x, _ = gap_x(tp8, shape, B, offset=300)
+    plan = make_plan(tp8, shape, B)
+    plan.set_profiling(True)
+    for _ in range(3):
+        out, idx, w, nu = run_gpu(plan, tp8, x, shape)
+    prof = plan.profile_read()
+    assert all(prof[k][1] == 3 and prof[k][0] > 0 for k in prof)
+    out64, idx_o, w_o = run_oracle(tp8, shape, x)
+    compare(out, idx, w, out64, idx_o, w_o, "profiled")
+    plan.destroy()
+
+
+# ----------------------------------------------------------- unsharded shape
+
+@pytest.fixture(scope="module")
+def full():
+    layer = DeviceLayer(synthetic.FULL)
+    yield layer
+    del layer
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("batch,sample", [(1, None), (16, [0, 7, 15]), (32, [0, 13, 31]),
+                                          (64, [0, 21, 42, 63])])
+def test_unsharded_sampled(full, batch, sample):
+    check(full, shape_of(synthetic.FULL), batch, "unsharded B=%d" % batch, sample=sample)
+
+
+# --------------------------------------------------------------- edge shapes
+
+EDGE = [
+    # name, H, E, k, I, Is, score, renorm, scale, bias, batch
+    ("one_expert_top1", 256, 1, 1, 128, 0, 1, 1, 1.0, False, 3),
+    ("no_shared", 512, 16, 4, 128, 0, 1, 1, 1.0, False, 5),
+    ("shared_two_blocks", 512, 16, 4, 128, 256, 1, 1, 1.0, False, 9),
+    ("inter64", 320, 12, 3, 64, 64, 0, 1, 1.0, False, 7),
+    ("inter512", 1024, 10, 2, 512, 512, 1, 1, 1.0, True, 11),
+    ("inter1024", 576, 6, 2, 1024, 2048, 1, 1, 1.0, False, 4),
+    ("hidden64", 64, 5, 2, 64, 64, 1, 1, 1.0, False, 2),
+    ("topk16", 256, 64, 16, 64, 64, 1, 1, 1.0, False, 6),
+    ("experts1024", 256, 1024, 8, 64, 0, 1, 1, 1.0, True, 20),
+    ("scaled_softmax_unnormalised", 256, 16, 4, 128, 128, 0, 0, 2.5, False, 12),
+    ("sigmoid_unnormalised", 256, 16, 4, 128, 128, 1, 0, 1.0, True, 12),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_shapes(case):
+    name, H, E, k, I, Is, score, ren, scale, bias, B = case
+    wl = synthetic.Workload(name, H, E, k, I, Is, B, score, router_std=0.05, weight_std=0.05,
+                            zipf_s=1.1 if bias else None, seed=3)
+    layer = DeviceLayer(wl, host=True)
+    shape = shape_of(wl, renormalize=ren, routed_scale=scale)
+    for b in sorted({1, B}):
+        check(layer, shape, b, "%s B=%d" % (name, b))
