@@ -74,6 +74,14 @@ typedef struct moe_decode_config {
     int32_t force_variant;   /* moe_variant                                           */
     int32_t mfma_min_tokens; /* SPLIT_K: token count from which an expert uses MFMA
                                 tiles; 0 = library default                           */
+    int32_t shared_stream;   /* 0: the shared expert's gate/up runs in trailing
+                                workgroups of the router launch (overlap without a
+                                second queue); 1: on the plan's second stream,
+                                forked before the router and joined before the down
+                                projection                                           */
+    int32_t topk_launch;     /* batch <= 4 only.  0: default; 1: top-k and bucketing
+                                in the router launch's last workgroup to arrive;
+                                2: in a launch of their own after the router         */
 } moe_decode_config;
 
 typedef struct moe_decode_plan_s* moe_decode_plan_t;
@@ -83,6 +91,8 @@ typedef struct moe_decode_info {
     int32_t n_kernels;        /* kernel launches per forward                            */
     int32_t mfma_min_tokens;  /* resolved threshold (SPLIT_K), else 0                   */
     int32_t shared_mfma;      /* 1 if the shared expert runs on MFMA tiles              */
+    int32_t shared_stream;    /* resolved shared_stream                                  */
+    int32_t router_mfma;      /* 1: router is a split-K MFMA launch + a top-k launch     */
     size_t workspace_bytes;   /* device workspace owned by the plan                     */
 } moe_decode_info;
 
@@ -109,12 +119,15 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
  *                                            ignored (may be NULL) when Is == 0
  *   out      bf16 [B][H]                     result, round-to-nearest-even;
  *                                            must not overlap x
- * The first call on a device allocates the plan's workspace, a second stream
- * and events, and records the launches into a HIP graph; later calls replay
- * the graph, updating kernel arguments when the pointers change.  Work is
- * enqueued on `stream` and the plan's private stream only; the call returns
- * once it is enqueued.  Calls on one plan must not overlap (they share the
- * workspace). */
+ * The first call on a device allocates the plan's workspace (zeroed with
+ * hipMemsetAsync on `stream`, so make the first call outside any graph
+ * capture), a second stream and events, and builds a HIP graph of the
+ * launches; later calls replay it, updating kernel arguments when the
+ * pointers change.  When `stream` is being captured the kernels are launched
+ * directly (and so recorded into the caller's graph, with no memset).  Work
+ * is enqueued on `stream` and the plan's private stream only; the call
+ * returns once it is enqueued.  Calls on one plan must not overlap (they
+ * share the workspace). */
 moe_status moe_decode_forward(moe_decode_plan_t plan, const void* x, const void* router_w,
                               const void* expert_w, const void* shared_w, void* out,
                               void* stream);

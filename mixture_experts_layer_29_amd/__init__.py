@@ -54,12 +54,14 @@ class Config(ctypes.Structure):
                 ("score_fn", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("routed_scale", ctypes.c_float), ("add_residual", ctypes.c_int32),
                 ("router_bias", ctypes.c_void_p), ("force_variant", ctypes.c_int32),
-                ("mfma_min_tokens", ctypes.c_int32)]
+                ("mfma_min_tokens", ctypes.c_int32), ("shared_stream", ctypes.c_int32),
+                ("topk_launch", ctypes.c_int32)]
 
 
 class Info(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("n_kernels", ctypes.c_int32),
                 ("mfma_min_tokens", ctypes.c_int32), ("shared_mfma", ctypes.c_int32),
+                ("shared_stream", ctypes.c_int32), ("router_mfma", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -127,9 +129,10 @@ def _stream(stream) -> int | None:
 
 def make_config(hidden, n_experts, top_k, inter, shared_inter, batch, score_fn=SIGMOID, renormalize=1,
                 routed_scale=1.0, add_residual=1, router_bias=None, force_variant=VARIANT_AUTO,
-                mfma_min_tokens=0) -> Config:
+                mfma_min_tokens=0, shared_stream=0, topk_launch=0) -> Config:
     return Config(hidden, n_experts, top_k, inter, shared_inter, batch, score_fn, renormalize,
-                  float(routed_scale), add_residual, _ptr(router_bias), force_variant, mfma_min_tokens)
+                  float(routed_scale), add_residual, _ptr(router_bias), force_variant, mfma_min_tokens,
+                  shared_stream, topk_launch)
 
 
 class Plan:

@@ -23,16 +23,25 @@ enum ErrBits : int { ERR_BUCKET = 1, ERR_TILE = 2 };
 constexpr int kMaxBatch = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
-constexpr int kSplitK = 16;        // K-splits of an MFMA gate/up tile group
+constexpr int kSplitK = 16;        // K-splits of an MFMA tile group
 constexpr int kPairsPerGemvTile = 4;
 constexpr int kPairsPerMfmaTile = 64;
+constexpr int kMaxGemvUnits = 16;  // 16-byte units per lane held in registers by a GEMV wave
+constexpr int kGemvLdsBytes = 60 * 1024;  // x staging budget of a GEMV workgroup
+constexpr int kRouterRowsPerMfmaTile = 64;
+constexpr int kDownHStage = 32 * 1024;  // LDS bytes for a staged batch of h rows in down
 
-// Router GEMV + top-k + routing weights + bucketing (one launch).
+// Router + top-k + routing weights + bucketing.  Batches up to 4 use one
+// launch (GEMV, last workgroup selects and buckets); larger batches use an
+// MFMA split-K launch accumulating into zacc and a per-token top-k launch
+// whose last workgroup buckets.
 struct RouterArgs {
     const uint16_t* x;      // bf16 [B][H]
     const uint16_t* wr;     // bf16 [E][H]
     const float* bias;      // fp32 [E] or null
     float* z;               // fp32 [B][E] logits (workspace)
+    float* zacc;            // fp32 [B][E] split-K partial logits (zero between uses)
+    int32_t ksplit, kslice; // MFMA router: K splits and K elements per split
     int32_t* topk_idx;      // [B][k]
     float* topk_w;          // [B][k]
     int32_t* meta;
@@ -62,6 +71,8 @@ struct GateUpArgs {
     uint32_t* tile_cnt;      // per (entry, row block) arrival counters (zero between uses)
     int32_t* meta;
     int32_t H, n;
+    int32_t n_experts;          // valid expert ids: [0, n_experts)
+    int32_t max_slots;          // valid slots: [0, max_slots)
     int32_t tiles_per_expert;   // grid.x = max entries * tiles_per_expert
     int32_t mfma_min_tokens;    // 0: GEMV only
     int32_t ksplit;             // K-splits per MFMA row block
@@ -83,6 +94,18 @@ struct DownArgs {
     uint16_t* out;           // bf16 [B][H]
     int32_t H, I, Is, B, k;
     int32_t add_residual;
+    int32_t n_experts;
+    int32_t h_in_lds;        // 1: all of h and hs are staged in LDS at kernel start
+};
+
+// First launch of a layer: the router (GEMV for batch <= 4, split-K MFMA
+// above) and, in its trailing workgroups, the shared expert's gate/up rows,
+// which need only x and so overlap routing without a second stream.
+struct FrontArgs {
+    RouterArgs r;
+    GateUpArgs s;           // shared expert work list (ignored when shared_blocks == 0)
+    int32_t router_blocks;  // workgroups [0, router_blocks) run the router
+    int32_t shared_blocks;  // workgroups [router_blocks, +shared_blocks) run the shared gate/up
 };
 
 // Writes the shared expert's constant work list (run once per workspace).
@@ -99,12 +122,20 @@ struct KernelPick {
     const void* func;
     dim3 grid;
     dim3 block;
+    size_t lds;  // dynamic LDS bytes
 };
 
 KernelPick pick_init(const InitArgs& a);
-KernelPick pick_router(const RouterArgs& a);
+// Front launch: batch <= 4 (router GEMV, with top-k + bucketing in the last
+// workgroup when select_in_router) or larger (router MFMA).  Otherwise top-k
+// and bucketing follow in pick_topk's launch.  shared_tb: 0 when the shared
+// expert uses MFMA tiles, else its GEMV token count.
+KernelPick pick_front(const FrontArgs& f, bool small_router, bool select_in_router, int shared_tb);
+int front_router_blocks(const RouterArgs& a, bool small_router);
+KernelPick pick_topk(const RouterArgs& a);
 KernelPick pick_gateup(const GateUpArgs& a, int max_entries, int gemv_tokens);
 KernelPick pick_down(const DownArgs& a);
 int down_rows_per_block(int I);
+size_t down_h_lds_bytes(int B, int k, int I, int Is);
 
 }  // namespace moe

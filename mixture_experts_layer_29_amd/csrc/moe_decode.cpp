@@ -4,14 +4,16 @@
 // GEMV at batch <= 2, split-K above: the shape choice the Kimi K3 decode
 // article describes in Part 1 section 1) and sizes the workspace; it touches
 // no device.  The first forward allocates the workspace, a second stream and
-// events, and builds a HIP graph with the router -> gate/up -> down chain and
-// the shared expert's gate/up as a parallel branch joined before the down
-// projection (article Part 1 section 3: shared expert on its own stream,
-// overlapped with routing; "What's next": per-step host work replayed as a
-// graph).  Later forwards replay the graph, patching kernel arguments when the
-// caller's pointers change.  The eager path launches the same kernels on the
-// caller's stream and the plan's second stream with fork/join events, and is
-// used for per-kernel timing.
+// events, and builds a HIP graph: front (router, and by default the shared
+// expert's gate/up in trailing workgroups) -> [top-k] -> routed gate/up ->
+// down.  With shared_stream = 1 the shared expert's gate/up is a parallel
+// branch on the second stream joined before the down projection instead
+// (article Part 1 section 3: shared expert on its own stream, overlapped with
+// routing; "What's next": per-step host work replayed as a graph).  Later
+// forwards replay the graph, patching kernel arguments when the caller's
+// pointers change; a forward on a capturing stream launches the kernels
+// directly so they land in the caller's graph.  The eager path is also used
+// for per-kernel timing.
 #include "../../include/moe_decode.h"
 
 #include <hip/hip_runtime.h>
@@ -51,16 +53,20 @@ moe_status fail(moe_status st, const char* fmt, ...) {
                         __FILE__, __LINE__);                                                  \
     } while (0)
 
-constexpr int kDefaultMfmaMin = 8;
+constexpr int kDefaultMfmaMin = 4;
 constexpr int kMaxProfiledForwards = 1024;
+constexpr int kSmallRouterMaxBatch = 4;
+constexpr size_t kSmallRouterLds = 56 * 1024;
 
-enum Slot { S_ROUTER = 0, S_GATEUP = 1, S_SHARED = 2, S_DOWN = 3, S_COUNT = 4 };
-const char* kSlotNames[S_COUNT] = {"router_topk", "gateup_routed", "gateup_shared", "down_combine"};
+constexpr size_t kDownHLds = 48 * 1024;
+
+enum Slot { S_FRONT = 0, S_TOPK = 1, S_GATEUP = 2, S_SHARED = 3, S_DOWN = 4, S_COUNT = 5 };
+const char* kSlotNames[S_COUNT] = {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine"};
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-    size_t meta, z, topk_idx, topk_w, act_e, act_off, perm, sh_act_e, sh_act_off, sh_perm;
+    size_t meta, z, zacc, topk_idx, topk_w, act_e, act_off, perm, sh_act_e, sh_act_off, sh_perm;
     size_t h, hs, g_acc, g_acc_s, tile_cnt, tile_cnt_s, total;
 };
 
@@ -74,6 +80,9 @@ struct moe_decode_plan_s {
     bool shared_mfma;
     int max_act;          // min(E, B*k)
     int ksplit, kslice;
+    bool small_router;    // batch <= 4: one router launch; else MFMA router + top-k launch
+    bool shared_stream;   // shared gate/up on the second stream instead of the front launch
+    bool select_in_router;// batch <= 4: top-k + bucketing in the router's last workgroup
     Layout L;
 
     // device state (first forward)
@@ -84,16 +93,20 @@ struct moe_decode_plan_s {
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
     // argument blocks; the pointer fields are refreshed per forward
-    RouterArgs ra{};
-    GateUpArgs ga{}, gs{};
+    FrontArgs fa{};
+    RouterArgs& ra = fa.r;
+    GateUpArgs& gs = fa.s;
+    GateUpArgs ga{};
     DownArgs da{};
-    KernelPick kr{}, kg{}, ks{}, kd{};
+    KernelPick kf{}, kt{}, kg{}, ks{}, kd{};
 
     // graph
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
-    hipGraphNode_t n_router = nullptr, n_gateup = nullptr, n_shared = nullptr, n_down = nullptr;
-    const void* baked[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    hipGraphNode_t n_front = nullptr, n_topk = nullptr, n_gateup = nullptr, n_shared = nullptr,
+                   n_down = nullptr;
+    const void* args_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // in the arg blocks
+    const void* graph_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};  // in the graph exec
     bool have_forward = false;
 
     // profiling
@@ -125,6 +138,10 @@ moe_status validate(const moe_decode_config* c) {
         return fail(MOE_ERR_INVALID, "force_variant %d is not a moe_variant", c->force_variant);
     if (c->mfma_min_tokens < 0)
         return fail(MOE_ERR_INVALID, "mfma_min_tokens must be >= 0");
+    if (c->shared_stream != 0 && c->shared_stream != 1)
+        return fail(MOE_ERR_INVALID, "shared_stream must be 0 or 1");
+    if (c->topk_launch < 0 || c->topk_launch > 2)
+        return fail(MOE_ERR_INVALID, "topk_launch must be 0, 1 or 2");
     if (c->router_bias && (reinterpret_cast<uintptr_t>(c->router_bias) & 3))
         return fail(MOE_ERR_INVALID, "router_bias must be 4-byte aligned");
     // shapes the kernels cover
@@ -154,6 +171,7 @@ Layout make_layout(const moe_decode_config& c, int max_act, bool split) {
     };
     L.meta = take(M_COUNT * 4);
     L.z = take(B * E * 4);
+    L.zacc = take(B * E * 4);
     L.topk_idx = take(B * k * 4);
     L.topk_w = take(B * k * 4);
     L.act_e = take((size_t)max_act * 4);
@@ -186,6 +204,9 @@ void fill_static_args(moe_decode_plan_s* p) {
     RouterArgs& r = p->ra;
     r.bias = c.router_bias;
     r.z = at<float>(p, p->L.z);
+    r.zacc = at<float>(p, p->L.zacc);
+    r.ksplit = p->ksplit;
+    r.kslice = p->kslice;
     r.topk_idx = at<int32_t>(p, p->L.topk_idx);
     r.topk_w = at<float>(p, p->L.topk_w);
     r.meta = at<int32_t>(p, p->L.meta);
@@ -216,6 +237,8 @@ void fill_static_args(moe_decode_plan_s* p) {
     g.meta = r.meta;
     g.H = c.hidden;
     g.n = c.inter;
+    g.n_experts = c.n_experts;
+    g.max_slots = c.batch * c.top_k;
     g.tiles_per_expert = c.inter / kPairsPerGemvTile;
     g.mfma_min_tokens = p->mfma_min;
     g.ksplit = p->ksplit;
@@ -235,13 +258,20 @@ void fill_static_args(moe_decode_plan_s* p) {
         s.meta = r.meta;
         s.H = c.hidden;
         s.n = c.shared_inter;
+        s.n_experts = 1;
+        s.max_slots = c.batch;
         s.tiles_per_expert = c.shared_inter / kPairsPerGemvTile;
         s.mfma_min_tokens = p->shared_mfma ? 1 : 0;
         s.ksplit = p->ksplit;
         s.kslice = p->kslice;
     }
 
+    p->fa.router_blocks = front_router_blocks(r, p->small_router);
+    p->fa.shared_blocks = (has_shared(p) && !p->shared_stream)
+                              ? c.shared_inter / kPairsPerGemvTile : 0;
+
     DownArgs& d = p->da;
+    d.h_in_lds = down_h_lds_bytes(c.batch, c.top_k, c.inter, c.shared_inter) <= kDownHLds ? 1 : 0;
     d.n_act = g.n_act;
     d.act_e = r.act_e;
     d.act_off = r.act_off;
@@ -255,6 +285,7 @@ void fill_static_args(moe_decode_plan_s* p) {
     d.B = c.batch;
     d.k = c.top_k;
     d.add_residual = c.add_residual;
+    d.n_experts = c.n_experts;
 }
 
 void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, const void* expert_w,
@@ -273,9 +304,10 @@ void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, con
     p->da.w2 = ew + (size_t)c.n_experts * 2 * c.inter * c.hidden;
     p->da.s2 = has_shared(p) ? sw + (size_t)2 * c.shared_inter * c.hidden : nullptr;
     p->da.out = static_cast<uint16_t*>(out);
-    p->kr = pick_router(p->ra);
+    p->kf = pick_front(p->fa, p->small_router, p->select_in_router, p->shared_mfma ? 0 : c.batch);
+    if (!p->select_in_router) p->kt = pick_topk(p->ra);
     p->kg = pick_gateup(p->ga, p->max_act, p->routed_gemv_tb);
-    if (has_shared(p)) p->ks = pick_gateup(p->gs, 1, c.batch);
+    if (has_shared(p) && p->shared_stream) p->ks = pick_gateup(p->gs, 1, p->shared_mfma ? 1 : c.batch);
     p->kd = pick_down(p->da);
 }
 
@@ -304,22 +336,23 @@ moe_status device_init(moe_decode_plan_s* p, hipStream_t stream) {
                 at<int32_t>(p, p->L.sh_perm), p->cfg.batch};
     KernelPick ki = pick_init(ia);
     void* args[] = {&ia};
-    HIP_TRY(hipLaunchKernel(ki.func, ki.grid, ki.block, args, 0, stream));
+    HIP_TRY(hipLaunchKernel(ki.func, ki.grid, ki.block, args, ki.lds, stream));
     p->ready = true;
     return MOE_OK;
 }
 
 moe_status launch(const KernelPick& k, void* args, hipStream_t s) {
     void* a[] = {args};
-    HIP_TRY(hipLaunchKernel(k.func, k.grid, k.block, a, 0, s));
+    HIP_TRY(hipLaunchKernel(k.func, k.grid, k.block, a, k.lds, s));
     return MOE_OK;
 }
 
-// Eager launch on the caller's stream and the plan's second stream.
+// Eager launch on the caller's stream (and, in shared_stream mode, the plan's
+// second stream).  ev: per-slot start/end events for timing, or null.
 moe_status enqueue_eager(moe_decode_plan_s* p, hipStream_t stream, hipEvent_t* ev) {
     moe_status st;
-    const bool sh = has_shared(p);
-    if (sh) {
+    const bool side = has_shared(p) && p->shared_stream;
+    if (side) {
         HIP_TRY(hipEventRecord(p->ev_fork, stream));
         HIP_TRY(hipStreamWaitEvent(p->s2, p->ev_fork, 0));
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_SHARED], p->s2));
@@ -327,13 +360,18 @@ moe_status enqueue_eager(moe_decode_plan_s* p, hipStream_t stream, hipEvent_t* e
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_SHARED + 1], p->s2));
         HIP_TRY(hipEventRecord(p->ev_join, p->s2));
     }
-    if (ev) HIP_TRY(hipEventRecord(ev[2 * S_ROUTER], stream));
-    if ((st = launch(p->kr, &p->ra, stream))) return st;
-    if (ev) HIP_TRY(hipEventRecord(ev[2 * S_ROUTER + 1], stream));
+    if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT], stream));
+    if ((st = launch(p->kf, &p->fa, stream))) return st;
+    if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT + 1], stream));
+    if (!p->select_in_router) {
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_TOPK], stream));
+        if ((st = launch(p->kt, &p->ra, stream))) return st;
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_TOPK + 1], stream));
+    }
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_GATEUP], stream));
     if ((st = launch(p->kg, &p->ga, stream))) return st;
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_GATEUP + 1], stream));
-    if (sh) HIP_TRY(hipStreamWaitEvent(stream, p->ev_join, 0));
+    if (side) HIP_TRY(hipStreamWaitEvent(stream, p->ev_join, 0));
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_DOWN], stream));
     if ((st = launch(p->kd, &p->da, stream))) return st;
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_DOWN + 1], stream));
@@ -346,24 +384,31 @@ hipKernelNodeParams node_params(const KernelPick& k, void** args) {
     np.gridDim = k.grid;
     np.func = const_cast<void*>(k.func);
     np.kernelParams = args;
-    np.sharedMemBytes = 0;
+    np.sharedMemBytes = (unsigned int)k.lds;
     np.extra = nullptr;
     return np;
 }
 
 moe_status build_graph(moe_decode_plan_s* p) {
     HIP_TRY(hipGraphCreate(&p->graph, 0));
+    void* af[] = {&p->fa};
     void* ar[] = {&p->ra};
     void* ag[] = {&p->ga};
     void* as[] = {&p->gs};
     void* ad[] = {&p->da};
-    hipKernelNodeParams np = node_params(p->kr, ar);
-    HIP_TRY(hipGraphAddKernelNode(&p->n_router, p->graph, nullptr, 0, &np));
+    hipKernelNodeParams np = node_params(p->kf, af);
+    HIP_TRY(hipGraphAddKernelNode(&p->n_front, p->graph, nullptr, 0, &np));
+    hipGraphNode_t route_done = p->n_front;
+    if (!p->select_in_router) {
+        np = node_params(p->kt, ar);
+        HIP_TRY(hipGraphAddKernelNode(&p->n_topk, p->graph, &p->n_front, 1, &np));
+        route_done = p->n_topk;
+    }
     np = node_params(p->kg, ag);
-    HIP_TRY(hipGraphAddKernelNode(&p->n_gateup, p->graph, &p->n_router, 1, &np));
+    HIP_TRY(hipGraphAddKernelNode(&p->n_gateup, p->graph, &route_done, 1, &np));
     hipGraphNode_t deps[2] = {p->n_gateup, nullptr};
     int ndeps = 1;
-    if (has_shared(p)) {
+    if (has_shared(p) && p->shared_stream) {
         np = node_params(p->ks, as);
         HIP_TRY(hipGraphAddKernelNode(&p->n_shared, p->graph, nullptr, 0, &np));
         deps[ndeps++] = p->n_shared;
@@ -375,15 +420,20 @@ moe_status build_graph(moe_decode_plan_s* p) {
 }
 
 moe_status patch_graph(moe_decode_plan_s* p) {
+    void* af[] = {&p->fa};
     void* ar[] = {&p->ra};
     void* ag[] = {&p->ga};
     void* as[] = {&p->gs};
     void* ad[] = {&p->da};
-    hipKernelNodeParams np = node_params(p->kr, ar);
-    HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_router, &np));
+    hipKernelNodeParams np = node_params(p->kf, af);
+    HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_front, &np));
+    if (!p->select_in_router) {
+        np = node_params(p->kt, ar);
+        HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_topk, &np));
+    }
     np = node_params(p->kg, ag);
     HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_gateup, &np));
-    if (has_shared(p)) {
+    if (has_shared(p) && p->shared_stream) {
         np = node_params(p->ks, as);
         HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_shared, &np));
     }
@@ -416,17 +466,28 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
     const moe_decode_config& c = p->cfg;
     p->variant = c.force_variant != MOE_VARIANT_AUTO ? c.force_variant
                  : (c.batch <= 2 ? MOE_VARIANT_SMALL_M : MOE_VARIANT_SPLIT_K);
+    // a GEMV tile stages its tokens' activations in LDS: at most this many tokens
+    const int gemv_cap = (int)(kGemvLdsBytes / ((size_t)2 * c.hidden));
     if (p->variant == MOE_VARIANT_SPLIT_K) {
         p->mfma_min = c.mfma_min_tokens ? c.mfma_min_tokens : kDefaultMfmaMin;
         if (p->mfma_min > kMaxBatch + 1) p->mfma_min = kMaxBatch + 1;
-        p->routed_gemv_tb = std::min(c.batch, p->mfma_min - 1);
-        if (p->routed_gemv_tb < 1) p->routed_gemv_tb = 1;
+        if (p->mfma_min > gemv_cap + 1) p->mfma_min = std::max(1, gemv_cap + 1);
+        p->routed_gemv_tb = std::max(1, std::min(c.batch, p->mfma_min - 1));
         p->shared_mfma = c.batch >= p->mfma_min;
     } else {
+        if (c.batch > gemv_cap) {
+            delete p;
+            return fail(MOE_ERR_UNSUPPORTED, "SMALL_M at batch %d needs %d bytes of LDS per workgroup "
+                        "(limit %d); use SPLIT_K", c.batch, 2 * c.batch * c.hidden, kGemvLdsBytes);
+        }
         p->mfma_min = 0;
         p->routed_gemv_tb = c.batch;
         p->shared_mfma = false;
     }
+    p->small_router = c.batch <= kSmallRouterMaxBatch &&
+                      (size_t)2 * c.batch * c.hidden <= kSmallRouterLds;
+    p->shared_stream = c.shared_stream != 0;
+    p->select_in_router = p->small_router && c.topk_launch != 2;
     p->max_act = std::min(c.n_experts, c.batch * c.top_k);
     // K split of an MFMA row block: the most splits <= 16 that divide H into multiples of 32
     p->ksplit = 1;
@@ -451,37 +512,45 @@ moe_status moe_decode_forward(moe_decode_plan_t p, const void* x, const void* ro
     const size_t act_bytes = (size_t)c.batch * c.hidden * 2;
     if (overlaps(x, act_bytes, out, act_bytes)) return fail(MOE_ERR_INVALID, "out overlaps x");
     hipStream_t stream = static_cast<hipStream_t>(stream_);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(stream, &cap));
+    if (cap == hipStreamCaptureStatusActive && !p->ready)
+        return fail(MOE_ERR_STATE, "the first forward of a plan allocates and zeroes its workspace; "
+                    "run it outside stream capture");
     moe_status st = device_init(p, stream);
     if (st) return st;
     if (!has_shared(p)) shared_w = nullptr;
     const void* tuple[5] = {x, router_w, expert_w, shared_w, out};
-    const bool changed = std::memcmp(tuple, p->baked, sizeof tuple) != 0;
-    if (changed || !p->have_forward) set_pointers(p, x, router_w, expert_w, shared_w, out);
+    if (!p->have_forward || std::memcmp(tuple, p->args_for, sizeof tuple) != 0) {
+        set_pointers(p, x, router_w, expert_w, shared_w, out);
+        std::memcpy(p->args_for, tuple, sizeof tuple);
+    }
     p->have_forward = true;
 
+    if (cap == hipStreamCaptureStatusActive) return enqueue_eager(p, stream, nullptr);  // into the caller's graph
     if (p->profiling) {
         if (p->prof_count >= kMaxProfiledForwards)
             return fail(MOE_ERR_STATE, "profiling records at most %d forwards", kMaxProfiledForwards);
         const size_t base = (size_t)p->prof_count * S_COUNT * 2;
         while (p->prof_events.size() < base + S_COUNT * 2) {
-            hipEvent_t ev;
-            HIP_TRY(hipEventCreate(&ev));
+            hipEvent_t ev;  // timing events without the system-scope fence (device-local timing)
+            HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableSystemFence));
             p->prof_events.push_back(ev);
         }
         st = enqueue_eager(p, stream, &p->prof_events[base]);
         if (st) return st;
         ++p->prof_count;
-        std::memcpy(p->baked, tuple, sizeof tuple);
         return MOE_OK;
     }
     if (!p->exec) {
         st = build_graph(p);
         if (st) return st;
-    } else if (changed) {
+        std::memcpy(p->graph_for, tuple, sizeof tuple);
+    } else if (std::memcmp(tuple, p->graph_for, sizeof tuple) != 0) {
         st = patch_graph(p);
         if (st) return st;
+        std::memcpy(p->graph_for, tuple, sizeof tuple);
     }
-    std::memcpy(p->baked, tuple, sizeof tuple);
     HIP_TRY(hipGraphLaunch(p->exec, stream));
     return MOE_OK;
 }
@@ -521,9 +590,11 @@ moe_status moe_decode_plan_info(moe_decode_plan_t p, moe_decode_info* info) {
     g_err.clear();
     if (!p || !info) return fail(MOE_ERR_INVALID, "NULL argument");
     info->variant = p->variant;
-    info->n_kernels = 3 + (p->cfg.shared_inter > 0 ? 1 : 0);
+    info->n_kernels = 3 + (p->select_in_router ? 0 : 1) + (has_shared(p) && p->shared_stream ? 1 : 0);
     info->mfma_min_tokens = p->mfma_min;
     info->shared_mfma = p->shared_mfma ? 1 : 0;
+    info->shared_stream = p->shared_stream ? 1 : 0;
+    info->router_mfma = p->small_router ? 0 : 1;
     info->workspace_bytes = p->L.total;
     return MOE_OK;
 }
@@ -555,7 +626,8 @@ moe_status moe_decode_profile_read(moe_decode_plan_t p, int32_t cap, double* tot
     if (p->prof_count == 0) return MOE_OK;
     for (int f = 0; f < p->prof_count; ++f) {
         for (int s = 0; s < S_COUNT && s < cap; ++s) {
-            if (s == S_SHARED && !has_shared(p)) continue;
+            if ((s == S_SHARED && !(has_shared(p) && p->shared_stream)) || (s == S_TOPK && p->select_in_router))
+                continue;
             hipEvent_t a = p->prof_events[((size_t)f * S_COUNT + s) * 2];
             hipEvent_t b = p->prof_events[((size_t)f * S_COUNT + s) * 2 + 1];
             HIP_TRY(hipEventSynchronize(b));

@@ -123,6 +123,21 @@ def bf16_round(a: np.ndarray) -> np.ndarray:
     return torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
 
 
+def compare_out(out_gpu: torch.Tensor, out64, label=""):
+    """The output rule alone (for replays where the routing accessor only
+    holds the last forward's routing)."""
+    og = out_gpu.float().cpu().double().numpy()
+    ref = bf16_round(out64)
+    err = np.abs(og - ref)
+    mae = float(err.mean())
+    rms = float(np.sqrt(np.mean(out64 ** 2)))
+    rel = float(np.max(err / np.maximum(np.abs(out64), 1e-2 * rms)))
+    assert np.all(np.isfinite(og)), label + ": non-finite output"
+    assert mae <= MAE_TOL, "%s: MAE %.3g > %g" % (label, mae, MAE_TOL)
+    assert rel <= REL_TOL, "%s: max rel %.3g > %g" % (label, rel, REL_TOL)
+    return {"mae": mae, "maxrel": rel}
+
+
 def compare(out_gpu: torch.Tensor, idx_g, w_g, out64, idx_o, w_o, label=""):
     B = out64.shape[0]
     for t in range(B):

@@ -66,6 +66,8 @@ def test_supported_configs_plan(kw):
     (dict(routed_scale=float("nan")), moe.MOE_ERR_INVALID),
     (dict(force_variant=3), moe.MOE_ERR_INVALID),
     (dict(mfma_min_tokens=-1), moe.MOE_ERR_INVALID),
+    (dict(shared_stream=2), moe.MOE_ERR_INVALID),
+    (dict(batch=64, force_variant=moe.VARIANT_SMALL_M), moe.MOE_ERR_UNSUPPORTED),
     (dict(router_bias=0x1002), moe.MOE_ERR_INVALID),
     (dict(hidden=7160), moe.MOE_ERR_UNSUPPORTED),
     (dict(hidden=16384 + 64), moe.MOE_ERR_UNSUPPORTED),
@@ -115,26 +117,36 @@ def test_auto_variant(batch, variant):
     p = moe.Plan(cfg(batch=batch))
     info = p.info()
     assert info.variant == variant
-    assert info.n_kernels == 4
+    # front (router + shared gate/up), [top-k], routed gate/up, down
+    assert info.router_mfma == (1 if batch > 4 else 0)
+    assert info.n_kernels == 3 + info.router_mfma
+    assert info.shared_stream == 0
     assert info.workspace_bytes > 0
     if variant == moe.VARIANT_SPLIT_K:
-        assert info.mfma_min_tokens == 8
-        assert info.shared_mfma == (1 if batch >= 8 else 0)
+        assert info.mfma_min_tokens == 4
+        assert info.shared_mfma == (1 if batch >= 4 else 0)
     else:
         assert info.mfma_min_tokens == 0 and info.shared_mfma == 0
+    p.destroy()
+    p = moe.Plan(cfg(batch=batch, shared_stream=1))
+    assert p.info().n_kernels == 4 + (1 if batch > 4 else 0) and p.info().shared_stream == 1
     p.destroy()
 
 
 def test_forced_variant_and_threshold():
-    p = moe.Plan(cfg(batch=64, force_variant=moe.VARIANT_SMALL_M))
+    p = moe.Plan(cfg(batch=4, force_variant=moe.VARIANT_SMALL_M))
     assert p.info().variant == moe.VARIANT_SMALL_M
     p.destroy()
     p = moe.Plan(cfg(batch=1, force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=1))
     i = p.info()
     assert i.variant == moe.VARIANT_SPLIT_K and i.mfma_min_tokens == 1 and i.shared_mfma == 1
     p.destroy()
-    p = moe.Plan(cfg(shared_inter=0))
+    p = moe.Plan(cfg(shared_inter=0, shared_stream=1))
     assert p.info().n_kernels == 3
+    p.destroy()
+    # the MFMA threshold is capped so a GEMV tile's activations fit in LDS
+    p = moe.Plan(cfg(hidden=16384, batch=16, mfma_min_tokens=10))
+    assert p.info().mfma_min_tokens == 2
     p.destroy()
 
 
@@ -142,7 +154,7 @@ def test_profiling_toggle_without_device():
     p = moe.Plan(cfg())
     p.set_profiling(True)
     prof = p.profile_read()
-    assert set(prof) == {"router_topk", "gateup_routed", "gateup_shared", "down_combine"}
+    assert set(prof) == {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine"}
     assert all(v == (0.0, 0) for v in prof.values())
     p.set_profiling(False)
     p.destroy()

@@ -12,7 +12,8 @@ import torch
 import mixture_experts_layer_29_amd as moe
 import oracle
 import synthetic
-from gpu_harness import DeviceLayer, compare, gap_x, make_plan, run_gpu, run_oracle, shape_of
+from gpu_harness import (DeviceLayer, compare, compare_out, gap_x, make_plan, run_gpu, run_oracle,
+                         shape_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +136,44 @@ def test_graph_replay_with_changing_inputs(tp8):
     plan.destroy()
 
 
+@pytest.mark.parametrize("batch", [1, 3, 16, 64])
+def test_tp8_shared_on_second_stream(tp8, batch):
+    shape = shape_of(synthetic.TP8)
+    m, st, info = check(tp8, shape, batch, "tp8 shared stream B=%d" % batch, shared_stream=1)
+    assert info.shared_stream == 1
+
+
+@pytest.mark.parametrize("batch,shared_stream", [(1, 0), (2, 1), (8, 0), (24, 1)])
+def test_forwards_captured_into_a_caller_graph(tp8, batch, shared_stream):
+    """Forwards recorded by torch's graph capture (the library launches its
+    kernels directly on a capturing stream) replay correctly, several times,
+    with eager work and synchronisation between the replays."""
+    shape = shape_of(synthetic.TP8)
+    plan = make_plan(tp8, shape, batch, shared_stream=shared_stream)
+    xs = [gap_x(tp8, shape, batch, offset=700 + 10 * i)[0] for i in range(3)]
+    xt = [synthetic.bits_to_torch_bf16(x, "cuda") for x in xs]
+    outs = [torch.empty_like(t) for t in xt]
+    plan.forward(xt[0], tp8.router_w, tp8.expert_w, tp8.shared_w, outs[0])  # allocates outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(3):
+            plan.forward(xt[i], tp8.router_w, tp8.expert_w, tp8.shared_w, outs[i])
+    refs = [run_oracle(tp8, shape, x)[0] for x in xs]
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            compare_out(outs[i], refs[i], "capture B=%d replay %d fwd %d" % (batch, rep, i))
+        assert torch.isfinite(junk)
+    assert plan.stats().error_flags == 0
+    plan.destroy()
+
+
 def test_profiling_path_matches(tp8):
     shape = shape_of(synthetic.TP8)
     B = 16
@@ -144,7 +183,9 @@ def test_profiling_path_matches(tp8):
     for _ in range(3):
         out, idx, w, nu = run_gpu(plan, tp8, x, shape)
     prof = plan.profile_read()
-    assert all(prof[k][1] == 3 and prof[k][0] > 0 for k in prof)
+    used = {k for k, v in prof.items() if v[1]}
+    assert used == {"front", "topk_bucket", "gateup_routed", "down_combine"}, prof
+    assert all(prof[k][1] == 3 and prof[k][0] > 0 for k in used)
     out64, idx_o, w_o = run_oracle(tp8, shape, x)
     compare(out, idx, w, out64, idx_o, w_o, "profiled")
     plan.destroy()
