@@ -81,13 +81,36 @@ __device__ __forceinline__ float dot8_f32(u32x4 w, const float4 h0, const float4
 
 // Wave-wide reductions through DPP (quad permutes, row mirrors, row
 // broadcasts 15/31); the result is read from lane 63 and is wave-uniform.
+// Lanes outside a step's row mask receive `old`: 0 for sums, v for max/min.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+    return dpp_i<CTRL, ROW_MASK>(v, v);
 }
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, dpp_i<CTRL, ROW_MASK>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f0(float v) {  // masked-off lanes read 0
+    return __builtin_bit_cast(float, dpp_i<CTRL, ROW_MASK>(0, __builtin_bit_cast(int, v)));
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64).  For G <= 16
+// every lane of a group gets the sum; for G = 32 and 64 the lanes of the
+// group's highest 16-lane row do (so lane G-1 of the group always has it).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (G >= 2) v += dpp_f0<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v += dpp_f0<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v += dpp_f0<0x141, 0xf>(v);  // row_half_mirror
+    if constexpr (G >= 16) v += dpp_f0<0x140, 0xf>(v); // row_mirror
+    if constexpr (G >= 32) v += dpp_f0<0x142, 0xa>(v); // row_bcast15 into rows 1, 3
+    if constexpr (G >= 64) v += dpp_f0<0x143, 0xc>(v); // row_bcast31 into rows 2, 3
+    return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -101,12 +124,7 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-    v += dpp_f<0xb1, 0xf>(v);
-    v += dpp_f<0x4e, 0xf>(v);
-    v += dpp_f<0x141, 0xf>(v);
-    v += dpp_f<0x140, 0xf>(v);
-    v += dpp_f<0x142, 0xa>(v);
-    v += dpp_f<0x143, 0xc>(v);
+    v = group_sum<64>(v);
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
@@ -138,13 +156,6 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total, i
     return *s_flag != 0;
 }
 
-// Sum over aligned groups of G lanes (G a power of two <= 64).
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
@@ -860,7 +871,7 @@ __device__ __forceinline__ void down_accum(const u32x4 (&wv)[RP][NQ], const floa
 #pragma unroll
         for (int q = 0; q < NQ; ++q) p = dot8_f32(wv[rp][q], h0[q], h1[q], p);
         p = group_sum<LPR>(p);
-        if (c == 0) s_acc[t * R + (rp * 4 + wave) * RW + rw] += wt * p;
+        if (c == LPR - 1) s_acc[t * R + (rp * 4 + wave) * RW + rw] += wt * p;
     }
 }
 
@@ -1002,7 +1013,7 @@ __global__ __launch_bounds__(256) void down_combine_kernel(DownArgs a) {
                 for (int q = 0; q < NQ; ++q) wa[ce][rp][q] = wb[ce][rp][q];
     }
     // the lane that accumulated (t, row) also writes it: no barrier needed
-    if (c == 0) {
+    if (c == LPR - 1) {
 #pragma unroll
         for (int rp = 0; rp < RP; ++rp) {
             const int rl = (rp * 4 + wave) * RW + rw;
