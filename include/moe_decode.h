@@ -82,6 +82,21 @@ typedef struct moe_decode_config {
     int32_t topk_launch;     /* batch <= 4 only.  0: default; 1: top-k and bucketing
                                 in the router launch's last workgroup to arrive;
                                 2: in a launch of their own after the router         */
+    int32_t single_launch;   /* 0 (default) or 1: the staged launches.  2: the whole
+                                layer as ONE persistent launch -- possible when
+                                batch <= 4, shared_stream = 0, topk_launch != 2 and
+                                the shape fits it (x and h staged in LDS), else
+                                MOE_ERR_UNSUPPORTED at plan time.  On MI355X it
+                                measured slower than the staged launches, so the
+                                default does not pick it.
+                                The single launch runs every stage -- router,
+                                selection, bucketing, shared and routed experts,
+                                combine -- as tasks that workgroups claim in
+                                dependency order, handing results over through
+                                device-scope counters; it assumes its workgroups
+                                (at most what fits on the GPU at once) are all
+                                resident, and each wait is bounded: a wait that
+                                runs out sets an error flag instead of hanging.   */
 } moe_decode_config;
 
 typedef struct moe_decode_plan_s* moe_decode_plan_t;
@@ -93,6 +108,8 @@ typedef struct moe_decode_info {
     int32_t shared_mfma;      /* 1 if the shared expert runs on MFMA tiles              */
     int32_t shared_stream;    /* resolved shared_stream                                  */
     int32_t router_mfma;      /* 1: router is a split-K MFMA launch + a top-k launch     */
+    int32_t single_launch;    /* 1: the layer runs as one persistent launch             */
+    int32_t layer_grid;       /* its workgroup count (0 until the first forward)        */
     size_t workspace_bytes;   /* device workspace owned by the plan                     */
 } moe_decode_info;
 
@@ -101,7 +118,9 @@ typedef struct moe_decode_stats {
     int32_t n_unique;         /* |U|: distinct routed experts selected in the step      */
     int32_t gemv_tiles;       /* routed gate/up tiles on the GEMV path                  */
     int32_t mfma_tiles;       /* routed gate/up tiles on the split-K MFMA path          */
-    int32_t error_flags;      /* 0 = no device-side error was detected                  */
+    int32_t error_flags;      /* 0 = no device-side error was detected; else bits: 1 an
+                                 invalid expert id reached the bucketing, 2 a work-list
+                                 entry was inconsistent, 4 a single-launch wait ran out */
 } moe_decode_stats;
 
 /* Validates `cfg` and builds a plan on the host.  Creates no device state, so
@@ -153,7 +172,7 @@ moe_status moe_decode_plan_info(moe_decode_plan_t plan, moe_decode_info* info);
  * per kernel slot, the summed milliseconds and the launch count over all
  * forwards since profiling was enabled (arrays of `cap` entries, host memory),
  * the slot names into `names` (may be NULL), and the slot count to *n.
- * At most 4096 forwards are recorded per enable. */
+ * At most 1024 forwards are recorded per enable. */
 moe_status moe_decode_set_profiling(moe_decode_plan_t plan, int32_t enable);
 moe_status moe_decode_profile_read(moe_decode_plan_t plan, int32_t cap, double* total_ms,
                                    int32_t* launches, const char** names, int32_t* n);

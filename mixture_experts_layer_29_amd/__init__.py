@@ -16,7 +16,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libmoe_decode.so")
 HEADER = os.path.join(_ROOT, "include", "moe_decode.h")
-SOURCES = [os.path.join(_HERE, "csrc", "moe_kernels.hip"), os.path.join(_HERE, "csrc", "moe_decode.cpp")]
+_CSRC = os.path.join(_HERE, "csrc")
+SOURCES = [os.path.join(_CSRC, f) for f in ("moe_kernels.hip", "moe_layer_tb1.hip", "moe_layer_tb2.hip",
+                                             "moe_layer_tb4.hip", "moe_decode.cpp")]
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_NOMEM, MOE_ERR_STATE = range(6)
 STATUS_NAMES = ["MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP", "MOE_ERR_NOMEM",
@@ -24,6 +26,7 @@ STATUS_NAMES = ["MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP
 SOFTMAX, SIGMOID = 0, 1
 VARIANT_AUTO, VARIANT_SMALL_M, VARIANT_SPLIT_K = 0, 1, 2
 VARIANT_NAMES = {0: "AUTO", 1: "SMALL_M", 2: "SPLIT_K"}
+SINGLE_AUTO, SINGLE_OFF, SINGLE_REQUIRED = 0, 1, 2
 
 EXPORTS = ["moe_decode_plan", "moe_decode_forward", "moe_decode_routing", "moe_decode_read_stats",
            "moe_decode_plan_info", "moe_decode_set_profiling", "moe_decode_profile_read",
@@ -31,13 +34,25 @@ EXPORTS = ["moe_decode_plan", "moe_decode_forward", "moe_decode_routing", "moe_d
 
 
 def build(arch: str = "gfx950", out: str = LIB_PATH, jobs: int = 8) -> str:
-    """Compile the HIP kernels and the host library into ``libmoe_decode.so``."""
+    """Compile the HIP kernels and the host library into ``libmoe_decode.so``
+    (one hipcc process per source file, ``jobs`` at a time, then one link)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    bdir = os.path.join(_HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    flags = ["--offload-arch=" + arch, "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall",
+             "-I", os.path.join(_ROOT, "include")]
+
+    def compile_one(src):
+        obj = os.path.join(bdir, os.path.basename(src) + ".o")
+        subprocess.run(["hipcc", *flags, "-c", src, "-o", obj], check=True)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["hipcc", "--offload-arch=" + arch, "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-parallel-jobs=%d" % jobs, "-Wall",
-           "-I", os.path.join(_ROOT, "include"), *SOURCES, "-o", tmp]
-    subprocess.run(cmd, check=True)
+    subprocess.run(["hipcc", "--offload-arch=" + arch, "-shared", "-fPIC", *objs, "-o", tmp], check=True)
     os.replace(tmp, out)
     return out
 
@@ -55,13 +70,14 @@ class Config(ctypes.Structure):
                 ("routed_scale", ctypes.c_float), ("add_residual", ctypes.c_int32),
                 ("router_bias", ctypes.c_void_p), ("force_variant", ctypes.c_int32),
                 ("mfma_min_tokens", ctypes.c_int32), ("shared_stream", ctypes.c_int32),
-                ("topk_launch", ctypes.c_int32)]
+                ("topk_launch", ctypes.c_int32), ("single_launch", ctypes.c_int32)]
 
 
 class Info(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("n_kernels", ctypes.c_int32),
                 ("mfma_min_tokens", ctypes.c_int32), ("shared_mfma", ctypes.c_int32),
                 ("shared_stream", ctypes.c_int32), ("router_mfma", ctypes.c_int32),
+                ("single_launch", ctypes.c_int32), ("layer_grid", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -129,10 +145,10 @@ def _stream(stream) -> int | None:
 
 def make_config(hidden, n_experts, top_k, inter, shared_inter, batch, score_fn=SIGMOID, renormalize=1,
                 routed_scale=1.0, add_residual=1, router_bias=None, force_variant=VARIANT_AUTO,
-                mfma_min_tokens=0, shared_stream=0, topk_launch=0) -> Config:
+                mfma_min_tokens=0, shared_stream=0, topk_launch=0, single_launch=SINGLE_AUTO) -> Config:
     return Config(hidden, n_experts, top_k, inter, shared_inter, batch, score_fn, renormalize,
                   float(routed_scale), add_residual, _ptr(router_bias), force_variant, mfma_min_tokens,
-                  shared_stream, topk_launch)
+                  shared_stream, topk_launch, single_launch)
 
 
 class Plan:

@@ -15,10 +15,17 @@ enum Meta : int {
     M_MFMA_TILES = 3,  // routed gate/up tiles that took the MFMA path
     M_ERR = 4,         // device-side error bits
     M_SHARED_NACT = 5, // constant 1: the shared expert's one-entry work list
+    // single-launch layer (all re-armed to 0 by the last workgroup to exit)
+    M_NEXT = 6,        // next dynamically claimed task
+    M_SGU_DONE = 7,    // shared gate/up tiles done
+    M_SDOWN_DONE = 8,  // shared down row blocks done
+    M_GU_DONE = 9,     // routed gate/up tiles done
+    M_SEL = 10,        // routing published
+    M_EXIT = 11,       // workgroups that left the task loop
     M_COUNT = 16
 };
 
-enum ErrBits : int { ERR_BUCKET = 1, ERR_TILE = 2 };
+enum ErrBits : int { ERR_BUCKET = 1, ERR_TILE = 2, ERR_TIMEOUT = 4 };
 
 constexpr int kMaxBatch = 64;
 constexpr int kMaxExperts = 1024;
@@ -92,6 +99,7 @@ struct DownArgs {
     const float* h;          // fp32 [B*k][I] routed h, slot-major
     const float* hs;         // fp32 [B][Is] shared h
     uint16_t* out;           // bf16 [B][H]
+    float* s_out;            // fp32 [B][H] shared-expert output (single-launch layer)
     int32_t H, I, Is, B, k;
     int32_t add_residual;
     int32_t n_experts;
@@ -106,6 +114,22 @@ struct FrontArgs {
     GateUpArgs s;           // shared expert work list (ignored when shared_blocks == 0)
     int32_t router_blocks;  // workgroups [0, router_blocks) run the router
     int32_t shared_blocks;  // workgroups [router_blocks, +shared_blocks) run the shared gate/up
+};
+
+// Whole layer in one launch (batch <= 4): tasks in dependency order
+// [router rows][shared gate/up][shared down][routed gate/up][routed down];
+// the first two groups are assigned by block index, the rest claimed in order.
+struct LayerArgs {
+    FrontArgs f;            // router (f.r) and shared gate/up list (f.s)
+    GateUpArgs g;           // routed gate/up
+    DownArgs d;             // down (shared part to d.s_out, then routed + finalize)
+    int32_t n_router;       // router tasks: 4 rows each
+    int32_t n_sgu;          // shared gate/up tasks
+    int32_t sgu_expect;     // shared gate/up tasks that do work
+    int32_t n_sdown;        // shared down tasks (row blocks)
+    int32_t n_gu;           // routed gate/up tasks (max entries * tiles per expert)
+    int32_t n_down;         // routed down tasks (row blocks)
+    int32_t shared_mfma;    // shared expert on MFMA tiles
 };
 
 // Writes the shared expert's constant work list (run once per workspace).
@@ -135,6 +159,8 @@ int front_router_blocks(const RouterArgs& a, bool small_router);
 KernelPick pick_topk(const RouterArgs& a);
 KernelPick pick_gateup(const GateUpArgs& a, int max_entries, int gemv_tokens);
 KernelPick pick_down(const DownArgs& a);
+// Single-launch layer; func is null when the shape has no instantiation.
+KernelPick pick_layer(const LayerArgs& L, size_t lds_bytes);
 int down_rows_per_block(int I);
 size_t down_h_lds_bytes(int B, int k, int I, int Is);
 

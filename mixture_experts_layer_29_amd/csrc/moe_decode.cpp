@@ -59,15 +59,17 @@ constexpr int kSmallRouterMaxBatch = 4;
 constexpr size_t kSmallRouterLds = 56 * 1024;
 
 constexpr size_t kDownHLds = 48 * 1024;
+constexpr size_t kLayerLds = 56 * 1024;  // dynamic LDS of the single launch: x staging, then h rows
 
-enum Slot { S_FRONT = 0, S_TOPK = 1, S_GATEUP = 2, S_SHARED = 3, S_DOWN = 4, S_COUNT = 5 };
-const char* kSlotNames[S_COUNT] = {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine"};
+enum Slot { S_FRONT = 0, S_TOPK = 1, S_GATEUP = 2, S_SHARED = 3, S_DOWN = 4, S_LAYER = 5, S_COUNT = 6 };
+const char* kSlotNames[S_COUNT] = {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine",
+                                   "layer"};
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
     size_t meta, z, zacc, topk_idx, topk_w, act_e, act_off, perm, sh_act_e, sh_act_off, sh_perm;
-    size_t h, hs, g_acc, g_acc_s, tile_cnt, tile_cnt_s, total;
+    size_t h, hs, g_acc, g_acc_s, tile_cnt, tile_cnt_s, s_out, total;
 };
 
 }  // namespace
@@ -83,6 +85,9 @@ struct moe_decode_plan_s {
     bool small_router;    // batch <= 4: one router launch; else MFMA router + top-k launch
     bool shared_stream;   // shared gate/up on the second stream instead of the front launch
     bool select_in_router;// batch <= 4: top-k + bucketing in the router's last workgroup
+    bool fused;           // the whole layer as one persistent launch
+    size_t layer_lds;     // its dynamic LDS bytes
+    int layer_grid = 0;   // its workgroups (set on the first forward)
     Layout L;
 
     // device state (first forward)
@@ -98,13 +103,14 @@ struct moe_decode_plan_s {
     GateUpArgs& gs = fa.s;
     GateUpArgs ga{};
     DownArgs da{};
-    KernelPick kf{}, kt{}, kg{}, ks{}, kd{};
+    LayerArgs la{};
+    KernelPick kf{}, kt{}, kg{}, ks{}, kd{}, kl{};
 
     // graph
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     hipGraphNode_t n_front = nullptr, n_topk = nullptr, n_gateup = nullptr, n_shared = nullptr,
-                   n_down = nullptr;
+                   n_down = nullptr, n_layer = nullptr;
     const void* args_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // in the arg blocks
     const void* graph_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};  // in the graph exec
     bool have_forward = false;
@@ -142,6 +148,8 @@ moe_status validate(const moe_decode_config* c) {
         return fail(MOE_ERR_INVALID, "shared_stream must be 0 or 1");
     if (c->topk_launch < 0 || c->topk_launch > 2)
         return fail(MOE_ERR_INVALID, "topk_launch must be 0, 1 or 2");
+    if (c->single_launch < 0 || c->single_launch > 2)
+        return fail(MOE_ERR_INVALID, "single_launch must be 0, 1 or 2");
     if (c->router_bias && (reinterpret_cast<uintptr_t>(c->router_bias) & 3))
         return fail(MOE_ERR_INVALID, "router_bias must be 4-byte aligned");
     // shapes the kernels cover
@@ -160,7 +168,7 @@ moe_status validate(const moe_decode_config* c) {
     return MOE_OK;
 }
 
-Layout make_layout(const moe_decode_config& c, int max_act, bool split) {
+Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fused) {
     const size_t B = c.batch, E = c.n_experts, k = c.top_k, I = c.inter, Is = c.shared_inter;
     Layout L{};
     size_t o = 0;
@@ -188,6 +196,7 @@ Layout make_layout(const moe_decode_config& c, int max_act, bool split) {
         L.tile_cnt = take((size_t)max_act * (I / kPairsPerMfmaTile) * 4);
         L.tile_cnt_s = take((Is / kPairsPerMfmaTile + 1) * 4);
     }
+    if (fused && Is) L.s_out = take(B * c.hidden * 4);
     L.total = o;
     return L;
 }
@@ -286,7 +295,24 @@ void fill_static_args(moe_decode_plan_s* p) {
     d.k = c.top_k;
     d.add_residual = c.add_residual;
     d.n_experts = c.n_experts;
+    d.s_out = (p->fused && has_shared(p)) ? at<float>(p, p->L.s_out) : nullptr;
+
+    if (p->fused) {
+        LayerArgs& l = p->la;
+        const int R = down_rows_per_block(c.inter);
+        l.n_router = (c.n_experts + 3) / 4;
+        l.n_sgu = has_shared(p) ? c.shared_inter / kPairsPerGemvTile : 0;
+        l.sgu_expect = !has_shared(p) ? 0
+                       : p->shared_mfma ? (c.shared_inter / kPairsPerMfmaTile) * p->ksplit
+                                        : c.shared_inter / kPairsPerGemvTile;
+        l.n_sdown = has_shared(p) ? c.hidden / R : 0;
+        l.n_gu = p->max_act * (c.inter / kPairsPerGemvTile);
+        l.n_down = c.hidden / R;
+        l.shared_mfma = p->shared_mfma ? 1 : 0;
+    }
 }
+
+int layer_tasks(const LayerArgs& l) { return l.n_router + l.n_sgu + l.n_sdown + l.n_gu + l.n_down; }
 
 void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, const void* expert_w,
                   const void* shared_w, void* out) {
@@ -309,6 +335,13 @@ void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, con
     p->kg = pick_gateup(p->ga, p->max_act, p->routed_gemv_tb);
     if (has_shared(p) && p->shared_stream) p->ks = pick_gateup(p->gs, 1, p->shared_mfma ? 1 : c.batch);
     p->kd = pick_down(p->da);
+    if (p->fused) {
+        p->la.f = p->fa;
+        p->la.g = p->ga;
+        p->la.d = p->da;
+        p->kl = pick_layer(p->la, p->layer_lds);
+        p->kl.grid = dim3(p->layer_grid);
+    }
 }
 
 moe_status device_init(moe_decode_plan_s* p, hipStream_t stream) {
@@ -337,6 +370,21 @@ moe_status device_init(moe_decode_plan_s* p, hipStream_t stream) {
     KernelPick ki = pick_init(ia);
     void* args[] = {&ia};
     HIP_TRY(hipLaunchKernel(ki.func, ki.grid, ki.block, args, ki.lds, stream));
+    if (p->fused) {
+        // every workgroup of the single launch must be resident at once: the grid is
+        // what the occupancy allows on this device, capped at the task count
+        const KernelPick k = pick_layer(p->la, p->layer_lds);
+        if (!k.func) return fail(MOE_ERR_UNSUPPORTED, "no single-launch kernel for this shape");
+        if (p->layer_lds > 64 * 1024)
+            HIP_TRY(hipFuncSetAttribute(k.func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p->layer_lds));
+        int per_cu = 0, cus = 0;
+        HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.func, 256, p->layer_lds));
+        HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+        if (per_cu < 1 || cus < 1)
+            return fail(MOE_ERR_UNSUPPORTED, "single-launch kernel does not fit a compute unit (%zu B LDS)",
+                        p->layer_lds);
+        p->layer_grid = std::min(layer_tasks(p->la), per_cu * cus);
+    }
     p->ready = true;
     return MOE_OK;
 }
@@ -351,6 +399,12 @@ moe_status launch(const KernelPick& k, void* args, hipStream_t s) {
 // second stream).  ev: per-slot start/end events for timing, or null.
 moe_status enqueue_eager(moe_decode_plan_s* p, hipStream_t stream, hipEvent_t* ev) {
     moe_status st;
+    if (p->fused) {
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_LAYER], stream));
+        if ((st = launch(p->kl, &p->la, stream))) return st;
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_LAYER + 1], stream));
+        return MOE_OK;
+    }
     const bool side = has_shared(p) && p->shared_stream;
     if (side) {
         HIP_TRY(hipEventRecord(p->ev_fork, stream));
@@ -391,6 +445,13 @@ hipKernelNodeParams node_params(const KernelPick& k, void** args) {
 
 moe_status build_graph(moe_decode_plan_s* p) {
     HIP_TRY(hipGraphCreate(&p->graph, 0));
+    if (p->fused) {
+        void* al[] = {&p->la};
+        hipKernelNodeParams np = node_params(p->kl, al);
+        HIP_TRY(hipGraphAddKernelNode(&p->n_layer, p->graph, nullptr, 0, &np));
+        HIP_TRY(hipGraphInstantiate(&p->exec, p->graph, nullptr, nullptr, 0));
+        return MOE_OK;
+    }
     void* af[] = {&p->fa};
     void* ar[] = {&p->ra};
     void* ag[] = {&p->ga};
@@ -420,6 +481,12 @@ moe_status build_graph(moe_decode_plan_s* p) {
 }
 
 moe_status patch_graph(moe_decode_plan_s* p) {
+    if (p->fused) {
+        void* al[] = {&p->la};
+        hipKernelNodeParams np = node_params(p->kl, al);
+        HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_layer, &np));
+        return MOE_OK;
+    }
     void* af[] = {&p->fa};
     void* ar[] = {&p->ra};
     void* ag[] = {&p->ga};
@@ -494,7 +561,30 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
     for (int s = kSplitK; s >= 1; --s)
         if (c.hidden % (32 * s) == 0) { p->ksplit = s; break; }
     p->kslice = c.hidden / p->ksplit;
-    p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K);
+    // single launch: batch <= 4, activations and every h row fit the LDS budget,
+    // a down shape with an instantiation (I = 64, 128, 256 or 512..2048)
+    {
+        const size_t x_lds = (size_t)2 * c.batch * c.hidden;
+        const size_t h_lds = down_h_lds_bytes(c.batch, c.top_k, c.inter, c.shared_inter);
+        const int ur = c.inter / 8;
+        const bool shape_ok = ur == 8 || ur == 16 || ur == 32 || (ur % 64 == 0 && ur / 64 <= 4);
+        const char* why = nullptr;
+        if (c.batch > kSmallRouterMaxBatch) why = "batch > 4";
+        else if (!p->small_router) why = "activations exceed the LDS budget";
+        else if (h_lds > kLayerLds) why = "the h rows exceed the LDS budget";
+        else if (!shape_ok) why = "no down shape for this inter";
+        else if (c.shared_stream) why = "shared_stream = 1 asks for the staged launches";
+        else if (c.topk_launch == 2) why = "topk_launch = 2 asks for the staged launches";
+        // measured slower than the staged launches on MI355X (one workgroup per
+        // CU and a latency-inflated critical path), so only on request
+        p->fused = c.single_launch == 2 && !why;
+        p->layer_lds = std::max(x_lds, h_lds);
+        if (c.single_launch == 2 && why) {
+            delete p;
+            return fail(MOE_ERR_UNSUPPORTED, "single_launch = 2: %s", why);
+        }
+    }
+    p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K, p->fused);
     *out_plan = p;
     return MOE_OK;
 }
@@ -590,11 +680,13 @@ moe_status moe_decode_plan_info(moe_decode_plan_t p, moe_decode_info* info) {
     g_err.clear();
     if (!p || !info) return fail(MOE_ERR_INVALID, "NULL argument");
     info->variant = p->variant;
-    info->n_kernels = 3 + (p->select_in_router ? 0 : 1) + (has_shared(p) && p->shared_stream ? 1 : 0);
+    info->n_kernels = p->fused ? 1 : 3 + (p->select_in_router ? 0 : 1) + (has_shared(p) && p->shared_stream ? 1 : 0);
     info->mfma_min_tokens = p->mfma_min;
     info->shared_mfma = p->shared_mfma ? 1 : 0;
     info->shared_stream = p->shared_stream ? 1 : 0;
     info->router_mfma = p->small_router ? 0 : 1;
+    info->single_launch = p->fused ? 1 : 0;
+    info->layer_grid = p->layer_grid;
     info->workspace_bytes = p->L.total;
     return MOE_OK;
 }
@@ -626,8 +718,10 @@ moe_status moe_decode_profile_read(moe_decode_plan_t p, int32_t cap, double* tot
     if (p->prof_count == 0) return MOE_OK;
     for (int f = 0; f < p->prof_count; ++f) {
         for (int s = 0; s < S_COUNT && s < cap; ++s) {
-            if ((s == S_SHARED && !(has_shared(p) && p->shared_stream)) || (s == S_TOPK && p->select_in_router))
-                continue;
+            const bool used = p->fused ? s == S_LAYER
+                              : !((s == S_SHARED && !(has_shared(p) && p->shared_stream)) ||
+                                  (s == S_TOPK && p->select_in_router) || s == S_LAYER);
+            if (!used) continue;
             hipEvent_t a = p->prof_events[((size_t)f * S_COUNT + s) * 2];
             hipEvent_t b = p->prof_events[((size_t)f * S_COUNT + s) * 2 + 1];
             HIP_TRY(hipEventSynchronize(b));

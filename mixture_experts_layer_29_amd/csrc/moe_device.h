@@ -1,0 +1,991 @@
+// moe_device.h -- gfx950 device code shared by the launches of the decode-time
+// MoE layer: load/dot/reduction helpers, top-k selection and routing weights,
+// bucketing, and the router, gate/up and down work units that the kernels in
+// moe_kernels.hip (one launch per stage) and moe_layer.h (the whole layer in
+// one launch) are built from.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "moe_args.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// acc + sum_{i<8} a_i * b_i over two vectors of 8 bf16 (v_dot2_f32_bf16).
+// The dword lanes are copied to scalars before the bit cast: hipcc 7.2 lowers
+// __builtin_bit_cast of an ext-vector member access (v.y) as element 0.
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
+    const uint32_t a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+    const uint32_t b0 = b[0], b1 = b[1], b2 = b[2], b3 = b[3];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a0), as_bf16x2(b0), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a1), as_bf16x2(b1), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a2), as_bf16x2(b2), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a3), as_bf16x2(b3), acc, false);
+    return acc;
+}
+
+// acc + sum_{i<8} w_i * h_i, w bf16, h fp32.
+__device__ __forceinline__ float dot8_f32(u32x4 w, const float4 h0, const float4 h1, float acc) {
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+    acc = fmaf(bf16_lo(w0), h0.x, acc);
+    acc = fmaf(bf16_hi(w0), h0.y, acc);
+    acc = fmaf(bf16_lo(w1), h0.z, acc);
+    acc = fmaf(bf16_hi(w1), h0.w, acc);
+    acc = fmaf(bf16_lo(w2), h1.x, acc);
+    acc = fmaf(bf16_hi(w2), h1.y, acc);
+    acc = fmaf(bf16_lo(w3), h1.z, acc);
+    acc = fmaf(bf16_hi(w3), h1.w, acc);
+    return acc;
+}
+
+// Wave-wide reductions through DPP (quad permutes, row mirrors, row
+// broadcasts 15/31); the result is read from lane 63 and is wave-uniform.
+// Lanes outside a step's row mask receive `old`: 0 for sums, v for max/min.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int v) {
+    return dpp_i<CTRL, ROW_MASK>(v, v);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, dpp_i<CTRL, ROW_MASK>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f0(float v) {  // masked-off lanes read 0
+    return __builtin_bit_cast(float, dpp_i<CTRL, ROW_MASK>(0, __builtin_bit_cast(int, v)));
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64).  For G <= 16
+// every lane of a group gets the sum; for G = 32 and 64 the lanes of the
+// group's highest 16-lane row do (so lane G-1 of the group always has it).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (G >= 2) v += dpp_f0<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v += dpp_f0<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v += dpp_f0<0x141, 0xf>(v);  // row_half_mirror
+    if constexpr (G >= 16) v += dpp_f0<0x140, 0xf>(v); // row_mirror
+    if constexpr (G >= 32) v += dpp_f0<0x142, 0xa>(v); // row_bcast15 into rows 1, 3
+    if constexpr (G >= 64) v += dpp_f0<0x143, 0xc>(v); // row_bcast31 into rows 2, 3
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<0xb1, 0xf>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f<0x4e, 0xf>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f<0x141, 0xf>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_f<0x140, 0xf>(v));  // row_mirror
+    v = fmaxf(v, dpp_f<0x142, 0xa>(v));  // row_bcast15
+    v = fmaxf(v, dpp_f<0x143, 0xc>(v));  // row_bcast31
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = group_sum<64>(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ int wave_min_int(int v) {
+    v = min(v, dpp_i<0xb1, 0xf>(v));
+    v = min(v, dpp_i<0x4e, 0xf>(v));
+    v = min(v, dpp_i<0x141, 0xf>(v));
+    v = min(v, dpp_i<0x140, 0xf>(v));
+    v = min(v, dpp_i<0x142, 0xa>(v));
+    v = min(v, dpp_i<0x143, 0xc>(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// A value every lane of the wave holds, made visibly wave-uniform (an SGPR):
+// branches and loop bounds on it stay scalar instead of being linearised
+// with exec masks, which would keep both sides' registers live together.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Data handed from one workgroup to another inside a launch (logits, routing,
+// work lists, h, partial sums, the shared-expert output) is written and read
+// only through these device-coherent accesses: relaxed agent-scope atomics,
+// which gfx950 issues with the sc1 (device scope) cache policy, so they are
+// performed where all 8 XCDs see them instead of in one XCD's L2.  A hand-off
+// is then: coherent stores, every wave waits for its stores to complete,
+// barrier, one relaxed counter update; the reader sees the counter, then
+// issues coherent loads.  This avoids agent-scope release/acquire fences,
+// which write back / invalidate a whole L2 and cost microseconds each when
+// many workgroups hand off at once.  Static data (weights, x, bias) is read
+// with ordinary cached loads.
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_dev(const int* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(unsigned* p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// four consecutive floats (16-byte aligned) as two coherent 64-bit loads
+__device__ __forceinline__ float4 ld_dev4(const float* p) {
+    const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
+    const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return float4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                  __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+}
+
+// Every wave's coherent stores have completed (and the compiler keeps later
+// memory operations after them); then the workgroup synchronises.
+__device__ __forceinline__ void stores_done_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
+// Counts this workgroup's arrival after its coherent stores completed;
+// returns true in the last of `total` workgroups to arrive, which may then
+// read every arriver's coherent stores.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total, int* s_flag) {
+    stores_done_barrier();
+    if (threadIdx.x == 0) {
+        const unsigned t = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = t == total - 1;
+    }
+    __syncthreads();
+    return uni(*s_flag) != 0;
+}
+
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// top-k selection, routing weights, bucketing
+// ---------------------------------------------------------------------------
+
+constexpr int kSlots = kMaxExperts / 64;  // logits held per lane
+constexpr int kNone = 0x7fffffff;
+
+// Top-k of one token by one wave.  Slot m of lane l holds the logit of expert
+// (slot0 + m * step) * 64 + l in v[m] (slots past E hold -inf and are never
+// selected).  Each round takes the wave-wide largest remaining logit (DPP
+// max); equal logits go to the lower expert id (ballot, then DPP min when
+// several lanes tie).  Fills sel_e / sel_z in rank order (wave-uniform);
+// rounds that find nothing left give sel_e = -1.
+template <int NS>
+__device__ __forceinline__ void topk_wave(const float (&v)[NS], int slot0, int step, int E, int k, int lane,
+                                          int (&sel_e)[kMaxTopK], float (&sel_z)[kMaxTopK]) {
+    uint32_t avail = 0;
+#pragma unroll
+    for (int m = 0; m < NS; ++m)
+        if ((slot0 + m * step) * 64 + lane < E) avail |= 1u << m;
+    float bv = -INFINITY;
+    int be = kNone;
+    auto lane_best = [&]() {
+        bv = -INFINITY;
+        be = kNone;
+#pragma unroll
+        for (int m = 0; m < NS; ++m)
+            if (((avail >> m) & 1u) && v[m] > bv) { bv = v[m]; be = (slot0 + m * step) * 64 + lane; }
+    };
+    lane_best();
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r) {
+        sel_e[r] = -1;
+        sel_z[r] = -INFINITY;
+        if (r < k) {
+            const float m = wave_max(bv);
+            const unsigned long long bal = __ballot(be != kNone && bv == m);
+            if (bal) {
+                int e;
+                if (__popcll(bal) == 1) e = __builtin_amdgcn_readlane(be, __ffsll(bal) - 1);
+                else e = wave_min_int(((bal >> lane) & 1ull) ? be : kNone);
+                sel_e[r] = e;
+                sel_z[r] = m;
+                if (lane == (e & 63)) {
+#pragma unroll
+                    for (int q = 0; q < NS; ++q)
+                        if ((slot0 + q * step) * 64 + lane == e) avail &= ~(1u << q);
+                    lane_best();
+                }
+            }
+        }
+    }
+}
+
+// Merges per-wave candidate lists (up to 64 (logit, expert) pairs, one per
+// lane; invalid lanes hold e = kNone) into the top-k, same order and ties.
+__device__ __forceinline__ void topk_merge(float cv, int ce, int k, int lane, int (&sel_e)[kMaxTopK],
+                                           float (&sel_z)[kMaxTopK]) {
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r) {
+        sel_e[r] = -1;
+        sel_z[r] = -INFINITY;
+        if (r < k) {
+            const float m = wave_max(cv);
+            const unsigned long long bal = __ballot(ce != kNone && cv == m);
+            if (bal) {
+                int e;
+                if (__popcll(bal) == 1) e = __builtin_amdgcn_readlane(ce, __ffsll(bal) - 1);
+                else e = wave_min_int(((bal >> lane) & 1ull) ? ce : kNone);
+                sel_e[r] = e;
+                sel_z[r] = m;
+                if (ce == e) { cv = -INFINITY; ce = kNone; }
+            }
+        }
+    }
+}
+
+// Routing weights of the selected logits (softmax or sigmoid, optional
+// renormalisation over the selection, times routed_scale); lane r < k
+// computes and writes entry r of the token's topk_idx / topk_w row (and of
+// s_pair_e when given).  zrow (the token's logits, readable by this wave) is
+// read only for a softmax without renormalisation, whose denominator runs
+// over all E experts.
+__device__ __forceinline__ void route_token(const RouterArgs& a, int t, int lane, const float* zrow,
+                                            const int (&sel_e)[kMaxTopK], const float (&sel_z)[kMaxTopK],
+                                            int32_t* s_pair_e) {
+    const int k = a.k, E = a.E;
+    float zr = -INFINITY;
+    int er = -1;
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r)
+        if (lane == r) { zr = sel_z[r]; er = sel_e[r]; }
+    const bool mine = lane < k;
+    const float m = sel_z[0];
+    float w;
+    if (a.score_fn == 0) {
+        const float ex = mine ? expf(zr - m) : 0.0f;
+        float den;
+        if (a.renormalize) {
+            den = wave_sum(ex);
+        } else {
+            float part = 0.0f;
+            for (int e = lane; e < E; e += 64) part += expf(ld_dev(zrow + e) - m);
+            den = wave_sum(part);
+        }
+        w = ex / den;
+    } else {
+        const float sg = mine ? 1.0f / (1.0f + expf(-zr)) : 0.0f;
+        w = a.renormalize ? sg / wave_sum(sg) : sg;
+    }
+    if (mine) {
+        st_dev(a.topk_idx + t * k + lane, er);
+        st_dev(a.topk_w + t * k + lane, w * a.routed_scale);
+        if (s_pair_e) s_pair_e[t * k + lane] = er;
+    }
+}
+
+// Writes the bucketing results common to both bucketing forms.
+__device__ __forceinline__ void bucket_meta(const RouterArgs& a, int nact, int nmfma, int npairs, int placed) {
+    if (placed != npairs) nact = nmfma = 0;  // invalid selection: no expert work at all
+    st_dev(a.act_off + nact, npairs);
+    st_dev(a.meta + M_NACT, nact);
+    st_dev(a.meta + M_MFMA_TILES, nmfma * a.mfma_tiles_per_expert);
+    st_dev(a.meta + M_GEMV_TILES, (nact - nmfma) * a.tiles_per_expert);
+    if (placed != npairs) atomicOr(&a.meta[M_ERR], ERR_BUCKET);
+    st_dev(a.meta + M_ROUTER_CNT, 0);  // re-armed for the next launch
+}
+
+// Bucketing by one wave for B*k <= 64 pairs (pair p in lane p): a pair's slot
+// is the number of pairs with a smaller (expert, pair) key, so slots are
+// ordered by expert then token; the first pair of each expert defines the
+// active-expert entry.  No barriers and no LDS atomics.
+__device__ __forceinline__ void bucket_wave(const RouterArgs& a, const int32_t* s_pair_e, int lane) {
+    const int np = a.B * a.k;
+    const int e = lane < np ? s_pair_e[lane] : kNone;
+    if (__ballot(lane < np && (e < 0 || e >= a.E))) {  // never hand an invalid id to the experts
+        if (lane == 0) bucket_meta(a, 0, 0, np, -1);
+        return;
+    }
+    int pos = 0, cnt = 0;
+    bool first = true;
+    for (int q = 0; q < np; ++q) {
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        pos += (eq < e || (eq == e && q < lane)) ? 1 : 0;
+        cnt += eq == e ? 1 : 0;
+        if (eq == e && q < lane) first = false;
+    }
+    if (lane < np) st_dev(a.perm + pos, lane);
+    const bool lead = lane < np && first;
+    const unsigned long long fm = __ballot(lead);
+    int apos = 0;
+    for (int q = 0; q < np; ++q) {
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        apos += (((fm >> q) & 1ull) && eq < e) ? 1 : 0;
+    }
+    if (lead) {
+        st_dev(a.act_e + apos, e);
+        st_dev(a.act_off + apos, pos);
+    }
+    const int nact = __popcll(fm);
+    const int nmfma = __popcll(__ballot(lead && a.mfma_min_tokens > 0 && cnt >= a.mfma_min_tokens));
+    if (lane == 0) bucket_meta(a, nact, nmfma, np, np);
+}
+
+// Exclusive scan over the 256 threads of the block of two counters at once.
+__device__ __forceinline__ void block_scan2(int v0, int v1, int* s_tmp, int& ex0, int& ex1, int& tot0, int& tot1) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int i0 = v0, i1 = v1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int o0 = __shfl_up(i0, d, 64), o1 = __shfl_up(i1, d, 64);
+        if (lane >= d) { i0 += o0; i1 += o1; }
+    }
+    if (lane == 63) { s_tmp[wave] = i0; s_tmp[4 + wave] = i1; }
+    __syncthreads();
+    int p0 = 0, p1 = 0;
+    for (int w = 0; w < wave; ++w) { p0 += s_tmp[w]; p1 += s_tmp[4 + w]; }
+    tot0 = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+    tot1 = s_tmp[4] + s_tmp[5] + s_tmp[6] + s_tmp[7];
+    ex0 = p0 + i0 - v0;
+    ex1 = p1 + i1 - v1;
+    __syncthreads();
+}
+
+// Bucketing by a 256-thread workgroup for up to 1024 pairs: LDS histogram
+// with a rank per pair, exclusive scan, scatter.  s_pair_e must hold the
+// selected ids; the order of pairs inside a bucket is unspecified.
+__device__ __forceinline__ void bucket_block(const RouterArgs& a, const int32_t* s_pair_e, int32_t* s_rank, int32_t* s_cnt,
+                             int32_t* s_tmp, int32_t* s_nmfma) {
+    const int tid = threadIdx.x, E = a.E;
+    for (int i = tid; i < E; i += 256) s_cnt[i] = 0;
+    if (tid == 0) *s_nmfma = 0;
+    __syncthreads();
+    const int npairs = a.B * a.k;
+    for (int p = tid; p < npairs; p += 256) {
+        const int e = s_pair_e[p];
+        s_rank[p] = (e >= 0 && e < E) ? atomicAdd(&s_cnt[e], 1) : -1;
+    }
+    __syncthreads();
+    // (an invalid id leaves ctot < npairs; bucket_meta then publishes an empty list)
+
+    constexpr int CH = kMaxExperts / 256;  // bins per thread
+    int cnt[CH], csum = 0, fsum = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int bin = tid * CH + c;
+        cnt[c] = (bin < E) ? s_cnt[bin] : 0;
+        csum += cnt[c];
+        fsum += cnt[c] > 0 ? 1 : 0;
+    }
+    int cex, fex, ctot, ftot;
+    block_scan2(csum, fsum, s_tmp, cex, fex, ctot, ftot);
+    int nm = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int bin = tid * CH + c;
+        if (bin < E) {
+            s_cnt[bin] = cex;  // becomes the bucket offset
+            if (cnt[c] > 0) {
+                st_dev(a.act_e + fex, bin);
+                st_dev(a.act_off + fex, cex);
+                if (a.mfma_min_tokens > 0 && cnt[c] >= a.mfma_min_tokens) ++nm;
+                ++fex;
+            }
+            cex += cnt[c];
+        }
+    }
+    if (nm) atomicAdd(s_nmfma, nm);
+    __syncthreads();
+    for (int p = tid; p < npairs; p += 256)
+        if (s_rank[p] >= 0) st_dev(a.perm + s_cnt[s_pair_e[p]] + s_rank[p], p);
+    if (tid == 0) bucket_meta(a, ftot, *s_nmfma, npairs, ctot);
+}
+
+// Selection for tokens t0 + wave of this workgroup.
+// src: per-token logit rows (E floats); with `from_acc` they are split-K
+// accumulators: the bias is added, the sum stored to a.z and the accumulator
+// cleared.  A single token is ranked by all four waves (each over every
+// fourth slot) and merged by wave 0.  Ends with a workgroup barrier, after
+// which s_pair_e (if given) holds the selected ids of the workgroup's tokens.
+template <int NS>
+__device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float* src, const float* bias,
+                                              bool from_acc, int32_t* s_pair_e, int32_t* s_cand_e,
+                                              float* s_cand_z, float* s_z) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.E, B = a.B, k = a.k;
+    int sel_e[kMaxTopK];
+    float sel_z[kMaxTopK];
+    auto fetch = [&](float* row, float* zout, int e) {
+        float v = ld_dev(row + e);
+        if (from_acc) {
+            v += bias ? bias[e] : 0.0f;
+            st_dev(zout + e, v);
+            st_dev(row + e, 0.0f);
+        }
+        return v;
+    };
+    if (B == 1) {
+        constexpr int NQ = (NS + 3) / 4;
+        float v[NQ];
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            const int e = (wave + 4 * m) * 64 + lane;
+            v[m] = (e < E) ? fetch(src, a.z, e) : -INFINITY;
+            if (e < E) s_z[e] = v[m];
+        }
+        topk_wave<NQ>(v, wave, 4, E, k, lane, sel_e, sel_z);
+        if (lane < k) {
+            int ce = kNone;
+            float cz = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < kMaxTopK; ++r)
+                if (lane == r) { ce = sel_e[r] >= 0 ? sel_e[r] : kNone; cz = sel_z[r]; }
+            s_cand_e[wave * kMaxTopK + lane] = ce;
+            s_cand_z[wave * kMaxTopK + lane] = cz;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const int r = lane % kMaxTopK;
+            const bool ok = r < k;
+            topk_merge(ok ? s_cand_z[lane] : -INFINITY, ok ? s_cand_e[lane] : kNone, k, lane, sel_e, sel_z);
+            route_token(a, 0, lane, s_z, sel_e, sel_z, s_pair_e);
+        }
+    } else {
+        const int t = t0 + wave;
+        if (t < B) {
+            float* row = src + (size_t)t * E;
+            float* zo = a.z + (size_t)t * E;
+            float v[NS];
+#pragma unroll
+            for (int m = 0; m < NS; ++m) {
+                const int e = m * 64 + lane;
+                v[m] = (e < E) ? fetch(row, zo, e) : -INFINITY;
+            }
+            topk_wave<NS>(v, 0, 1, E, k, lane, sel_e, sel_z);
+            // a full softmax reads the token's logits back: from_acc rows are in a.z (this
+            // wave's stores, complete after the wait)
+            __builtin_amdgcn_s_waitcnt(0);
+            route_token(a, t, lane, from_acc ? zo : row, sel_e, sel_z, s_pair_e);
+        }
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// front launch, batch <= 4: router GEMV + (last workgroup) top-k and bucketing,
+// plus the shared expert's gate/up in trailing workgroups
+// ---------------------------------------------------------------------------
+
+template <int TB>
+__device__ __forceinline__ void gemv_gateup_tile(const GateUpArgs& a, const uint16_t* W, int off, int T, int local,
+                                 uint16_t* s_x);
+template <int NTM>
+__device__ __forceinline__ bool mfma_gateup_tile(const GateUpArgs& a, const uint16_t* W, int entry, int off, int T, int local);
+
+// Router rows of block `blk` (one row per wave) for all B tokens: x staged in
+// LDS while the row loads are in flight; z = x . Wr[e] (+ bias) -- or the raw
+// sum into zacc when the selection runs in a later launch.
+template <int TB, bool TO_Z>
+__device__ __forceinline__ void router_rows(const RouterArgs& a, int blk, uint16_t* s_x) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H, E = a.E, B = a.B;
+    const int units = H >> 3, nu = (units + 63) >> 6;
+    const int e = blk * 4 + wave;
+    const bool row_ok = e < E;
+    const uint16_t* wrow = a.wr + (size_t)(row_ok ? e : 0) * H;
+    const u32x4 zero = u32x4{0, 0, 0, 0};
+
+    float acc[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
+    for (int base = 0; base < nu; base += kMaxGemvUnits) {
+        u32x4 w[kMaxGemvUnits];
+#pragma unroll
+        for (int q = 0; q < kMaxGemvUnits; ++q) {
+            const int u = (base + q) * 64 + lane;
+            w[q] = (row_ok && u < units) ? ld16(wrow + u * 8) : zero;
+        }
+        if (base == 0) {  // stage x while the weight loads are in flight
+            for (int i = tid; i < B * units; i += 256) {
+                const int t = i / units, u = i - t * units;
+                st16(s_x + t * H + u * 8, ld16(a.x + (size_t)t * H + u * 8));
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int q = 0; q < kMaxGemvUnits; ++q) {
+            const int u = (base + q) * 64 + lane;
+            if (base + q < nu && u < units) {
+#pragma unroll
+                for (int t = 0; t < TB; ++t)
+                    if (t < B) acc[t] = dot8(w[q], ld16(s_x + t * H + u * 8), acc[t]);
+            }
+        }
+    }
+    if (row_ok) {
+        const float b = a.bias ? a.bias[e] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            if (t < B) {
+                const float s = wave_sum(acc[t]);
+                if (lane == 0) {
+                    if constexpr (TO_Z) st_dev(a.z + (size_t)t * E + e, s + b);
+                    else st_dev(a.zacc + (size_t)t * E + e, s);
+                }
+            }
+        }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// front launch, batch > 4: split-K MFMA router GEMM into zacc, plus the
+// shared expert's gate/up in trailing workgroups; then topk_bucket
+// ---------------------------------------------------------------------------
+
+// Tile: 64 router rows (16 per wave) x one K slice x all B tokens.
+// A = router rows (16 x 32), B = x^T (32 x 16 tokens), fp32 atomics into zacc.
+__device__ __forceinline__ void router_mfma_tile(const RouterArgs& a, int tile) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int H = a.H, E = a.E, B = a.B;
+    const int r0 = (tile / a.ksplit) * kRouterRowsPerMfmaTile + wave * 16;
+    const int tl = lane & 15, kq = lane >> 4;
+    const int kbeg = (tile % a.ksplit) * a.kslice;
+    const int nsteps = min(a.kslice, H - kbeg) >> 5;
+    const int NT = (B + 15) >> 4;
+    const bool rok = r0 + tl < E;
+    const uint16_t* ar = a.wr + (size_t)(rok ? r0 + tl : 0) * H + kbeg + 8 * kq;
+    const uint16_t* xr[4];
+    bool xok[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int t = tt * 16 + tl;
+        xok[tt] = t < B;
+        xr[tt] = a.x + (size_t)(xok[tt] ? t : 0) * H + kbeg + 8 * kq;
+    }
+    const u32x4 zero = u32x4{0, 0, 0, 0};
+    f32x4 c[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) c[tt] = f32x4{0, 0, 0, 0};
+    for (int s = 0; s < nsteps; s += 4) {
+        u32x4 A[4], X[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool sok = s + u < nsteps;
+            A[u] = (sok && rok) ? ld16(ar + 32 * (s + u)) : zero;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                X[u][tt] = (sok && tt < NT && xok[tt]) ? ld16(xr[tt] + 32 * (s + u)) : zero;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                if (s + u < nsteps && tt < NT)
+                    c[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[u]),
+                                                                    __builtin_bit_cast(bf16x8, X[u][tt]),
+                                                                    c[tt], 0, 0, 0);
+    }
+    // D layout: lane holds rows 4*(lane/16)+r, column (token) lane%16
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int t = tt * 16 + tl;
+        if (tt < NT && t < B) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = r0 + 4 * kq + r;
+                if (row < E) atomicAdd(&a.zacc[(size_t)t * E + row], c[tt][r]);
+            }
+        }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// gateup
+// ---------------------------------------------------------------------------
+
+// Full-K GEMV tile: wave w computes row pair i = 4*local + w (gate row i and
+// up row n+i) for the entry's T <= TB tokens, whose activations the workgroup
+// stages in LDS after issuing its weight loads.
+template <int TB>
+__device__ __forceinline__ void gemv_gateup_tile(const GateUpArgs& a, const uint16_t* W, int off, int T, int local,
+                                 uint16_t* s_x) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H, n = a.n, units = H >> 3, nu = (units + 63) >> 6;
+    const int i = local * kPairsPerGemvTile + wave;
+    const uint16_t* g = W + (size_t)i * H;
+    const uint16_t* u = W + (size_t)(n + i) * H;
+    const u32x4 zero = u32x4{0, 0, 0, 0};
+    float ag[TB], au[TB];
+#pragma unroll
+    for (int j = 0; j < TB; ++j) { ag[j] = 0.0f; au[j] = 0.0f; }
+    for (int base = 0; base < nu; base += kMaxGemvUnits) {
+        u32x4 wg[kMaxGemvUnits], wu[kMaxGemvUnits];
+#pragma unroll
+        for (int q = 0; q < kMaxGemvUnits; ++q) {
+            const int uu = (base + q) * 64 + lane;
+            const bool ok = uu < units;
+            wg[q] = ok ? ld16(g + uu * 8) : zero;
+            wu[q] = ok ? ld16(u + uu * 8) : zero;
+        }
+        if (base == 0) {  // stage the tokens' activations while the weights stream in
+            for (int idx = tid; idx < T * units; idx += 256) {
+                const int j = idx / units, uu = idx - j * units;
+                const int tok = ld_dev(a.perm + off + j) / a.pair_div;
+                st16(s_x + j * H + uu * 8, ld16(a.x + (size_t)tok * H + uu * 8));
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int q = 0; q < kMaxGemvUnits; ++q) {
+            const int uu = (base + q) * 64 + lane;
+            if (base + q < nu && uu < units) {
+#pragma unroll
+                for (int j = 0; j < TB; ++j) {
+                    if (j < T) {
+                        const u32x4 xv = ld16(s_x + j * H + uu * 8);
+                        ag[j] = dot8(wg[q], xv, ag[j]);
+                        au[j] = dot8(wu[q], xv, au[j]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+        if (j < T) {
+            const float gs = wave_sum(ag[j]);
+            const float us = wave_sum(au[j]);
+            if (lane == 0) st_dev(a.h + (size_t)(off + j) * n + i, silu_f(gs) * us);
+        }
+    }
+}
+
+// Split-K MFMA tile: 64 row pairs (16 per wave) x one K slice x T <= 16*NTM
+// tokens (NTM 16-token column tiles; a small NTM keeps the register budget
+// small where the token count is known to be small).
+// A = weight rows (16 x 32), B = x^T (32 x 16 tokens); fp32 partials are
+// added to g_acc; the last of the `ksplit` tiles of the row block applies
+// SiLU*up, writes h and clears g_acc and its counter.
+template <int NTM>
+__device__ __forceinline__ bool mfma_gateup_tile(const GateUpArgs& a, const uint16_t* W, int entry, int off, int T,
+                                 int local) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H, n = a.n;
+    const int nrb = n / kPairsPerMfmaTile;
+    const int rb = local / a.ksplit, ks = local % a.ksplit;
+    if (rb >= nrb) return false;
+    const int i0 = rb * kPairsPerMfmaTile + wave * 16;
+    const int kbeg = ks * a.kslice;
+    const int nsteps = min(a.kslice, H - kbeg) >> 5;
+    const int tl = lane & 15, kq = lane >> 4;
+    const int NT = (T + 15) >> 4;
+
+    const uint16_t* xrow[NTM];
+    bool xok[NTM];
+#pragma unroll
+    for (int tt = 0; tt < NTM; ++tt) {
+        const int j = tt * 16 + tl;
+        xok[tt] = j < T;
+        xrow[tt] = a.x + (size_t)(xok[tt] ? ld_dev(a.perm + off + j) / a.pair_div : 0) * H + kbeg + 8 * kq;
+    }
+    const uint16_t* gr = W + (size_t)(i0 + tl) * H + kbeg + 8 * kq;
+    const uint16_t* ur = W + (size_t)(n + i0 + tl) * H + kbeg + 8 * kq;
+    const u32x4 zero = u32x4{0, 0, 0, 0};
+    f32x4 cg[NTM], cu[NTM];
+#pragma unroll
+    for (int tt = 0; tt < NTM; ++tt) { cg[tt] = f32x4{0, 0, 0, 0}; cu[tt] = f32x4{0, 0, 0, 0}; }
+    for (int s = 0; s < nsteps; s += 4) {
+        u32x4 Ag[4], Au[4], X[4][NTM];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool sok = s + u < nsteps;
+            Ag[u] = sok ? ld16(gr + 32 * (s + u)) : zero;
+            Au[u] = sok ? ld16(ur + 32 * (s + u)) : zero;
+#pragma unroll
+            for (int tt = 0; tt < NTM; ++tt)
+                X[u][tt] = (sok && tt < NT && xok[tt]) ? ld16(xrow[tt] + 32 * (s + u)) : zero;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int tt = 0; tt < NTM; ++tt) {
+                if (s + u < nsteps && tt < NT) {
+                    const bf16x8 Bx = __builtin_bit_cast(bf16x8, X[u][tt]);
+                    cg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Ag[u]), Bx,
+                                                                     cg[tt], 0, 0, 0);
+                    cu[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Au[u]), Bx,
+                                                                     cu[tt], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // D layout: lane holds rows 4*(lane/16)+r, column (token) lane%16
+    const int n2 = 2 * n;
+#pragma unroll
+    for (int tt = 0; tt < NTM; ++tt) {
+        const int j = tt * 16 + tl;
+        if (tt < NT && j < T) {
+            float* gp = a.g_acc + (size_t)(off + j) * n2 + i0 + 4 * kq;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                atomicAdd(gp + r, cg[tt][r]);
+                atomicAdd(gp + n + r, cu[tt][r]);
+            }
+        }
+    }
+    __shared__ int s_flag;
+    if (!arrive_last(&a.tile_cnt[entry * nrb + rb], (unsigned)a.ksplit, &s_flag)) return true;
+    const int rows = kPairsPerMfmaTile;
+    for (int idx = tid; idx < rows * T; idx += 256) {
+        const int j = idx / rows, i = rb * rows + idx % rows;
+        float* gp = a.g_acc + (size_t)(off + j) * n2;
+        const float g = ld_dev(gp + i), u = ld_dev(gp + n + i);
+        st_dev(a.h + (size_t)(off + j) * n + i, silu_f(g) * u);
+        st_dev(gp + i, 0.0f);
+        st_dev(gp + n + i, 0.0f);
+    }
+    if (tid == 0) st_dev(a.tile_cnt + entry * nrb + rb, 0u);
+    return true;
+}
+
+
+// ---------------------------------------------------------------------------
+// down
+// ---------------------------------------------------------------------------
+
+// LPR lanes share one W2 row (LPR = min(I/8, 64)); each lane loads NQ 16-byte
+// units per row; a wave covers 64/LPR rows per pass and RP passes; the
+// workgroup covers R = RP * 4 * (64/LPR) consecutive output rows.  Entries
+// (active routed experts, then Is/I column blocks of the shared expert) are
+// processed CE at a time, the next chunk's weights requested before the
+// current chunk is used.
+template <int LPR, int NQ, int RP>
+struct DownShape {
+    static constexpr int RW = 64 / LPR;
+    static constexpr int R = RP * 4 * RW;
+    static constexpr int CE = (16 / (RP * NQ)) > 0 ? 16 / (RP * NQ) : 1;
+};
+
+template <int LPR, int NQ, int RP>
+__device__ __forceinline__ void down_accum(const u32x4 (&wv)[RP][NQ], const float* hrow, float wt, int t,
+                                           int wave, int lane, float* s_acc) {
+    constexpr int RW = 64 / LPR;
+    constexpr int R = DownShape<LPR, NQ, RP>::R;
+    const int rw = lane / LPR, c = lane % LPR;
+    float4 h0[NQ], h1[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const float4* hp = reinterpret_cast<const float4*>(hrow + 8 * (c + LPR * q));
+        h0[q] = hp[0];
+        h1[q] = hp[1];
+    }
+#pragma unroll
+    for (int rp = 0; rp < RP; ++rp) {
+        float p = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) p = dot8_f32(wv[rp][q], h0[q], h1[q], p);
+        p = group_sum<LPR>(p);
+        if (c == LPR - 1) s_acc[t * R + (rp * 4 + wave) * RW + rw] += wt * p;
+    }
+}
+
+enum DownMode : int {
+    DOWN_ALL = 0,     // routed experts + shared column blocks, bf16 out (+ residual)
+    DOWN_SHARED = 1,  // shared column blocks only, fp32 result to s_out
+    DOWN_ROUTED = 2   // routed experts only; finalize adds s_out (+ residual)
+};
+
+// Down projection of one block of R output rows (row_block), see DownShape.
+// HLDS: every h row the block needs is copied to LDS once, overlapped with the
+// first chunk of weight loads; otherwise h is staged chunk by chunk.
+// wait() runs after the first chunk of (static) weights is requested and
+// before any h is read: the single-launch layer blocks there until the gate/up
+// tasks are done.  s_h: dynamic LDS; s_acc: kMaxBatch * R floats of LDS.
+template <int LPR, int NQ, int RP, bool HLDS, int MODE, class Wait>
+__device__ __forceinline__ void down_rows(const DownArgs& a, int row_block, float* s_h, float* s_acc, Wait&& wait) {
+    constexpr int mode = MODE;
+    // routing, work lists and h come from an earlier launch (DOWN_ALL: plain
+    // cached loads) or from other workgroups of this launch (coherent loads)
+    constexpr bool COH = MODE != DOWN_ALL;
+    auto ldi = [](const int* p) { if constexpr (COH) return ld_dev(p); else return *p; };
+    auto ldf = [](const float* p) { if constexpr (COH) return ld_dev(p); else return *p; };
+    auto ld4 = [](const float* p) {
+        if constexpr (COH) return ld_dev4(p);
+        else return *reinterpret_cast<const float4*>(p);
+    };
+    using S = DownShape<LPR, NQ, RP>;
+    constexpr int RW = S::RW, R = S::R, CE = S::CE;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H, I = a.I, B = a.B, k = a.k;
+    const int row0 = row_block * R;
+    const int rw = lane / LPR, c = lane % LPR;
+
+    const int nact = mode == DOWN_SHARED ? 0 : uni(ldi(a.n_act));
+    const int nsh = (mode == DOWN_ROUTED || !a.s2) ? 0 : a.Is / I;
+    const int total = nact + nsh;
+    const size_t estride = (size_t)H * I;
+
+    auto load_chunk = [&](int c0, u32x4 (&buf)[CE][RP][NQ]) {
+#pragma unroll
+        for (int ce = 0; ce < CE; ++ce) {
+            const int ent = c0 + ce;
+            if (ent < total) {
+                const uint16_t* w;
+                int ld;
+                if (ent < nact) {
+                    int ee = uni(ldi(a.act_e + ent));
+                    if ((unsigned)ee >= (unsigned)a.n_experts) ee = 0;  // bucketing never publishes this
+                    w = a.w2 + (size_t)ee * estride;
+                    ld = I;
+                } else {
+                    w = a.s2 + (size_t)(ent - nact) * I;
+                    ld = a.Is;
+                }
+#pragma unroll
+                for (int rp = 0; rp < RP; ++rp) {
+                    const int r = row0 + (rp * 4 + wave) * RW + rw;
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) buf[ce][rp][q] = ld16(w + (size_t)r * ld + 8 * (c + LPR * q));
+                }
+            }
+        }
+    };
+
+    u32x4 wa[CE][RP][NQ], wb[CE][RP][NQ];
+    load_chunk(0, wa);
+    for (int i = tid; i < B * R; i += 256) s_acc[i] = 0.0f;
+    wait();
+    // LDS layout when HLDS: routed h rows [B*k][I], then shared rows [B][Is]
+    const size_t hs_off = (size_t)B * k * I;
+    if constexpr (HLDS) {
+        const int nh = nact ? B * k * I / 4 : 0, nhs = nsh ? B * a.Is / 4 : 0;
+        float4* d = reinterpret_cast<float4*>(s_h);
+        for (int i = tid; i < nh; i += 256) d[i] = ld4(a.h + 4 * i);
+        for (int i = tid; i < nhs; i += 256) d[hs_off / 4 + i] = ld4(a.hs + 4 * i);
+    }
+    __syncthreads();
+
+    // copies h rows [r0, r1) (row i at src + i * ld) into s_h, I floats per row
+    auto stage_rows = [&](const float* src, size_t ld, int r0, int r1) {
+        const int per = I / 4;
+        float4* d = reinterpret_cast<float4*>(s_h);
+        for (int i = tid; i < (r1 - r0) * per; i += 256) {
+            const int r = i / per, c4 = i - r * per;
+            d[i] = ld4(src + (size_t)(r0 + r) * ld + 4 * c4);
+        }
+    };
+    const int PB = (kDownHStage / 4) / I;  // h rows per staged batch
+
+    for (int c0 = 0; c0 < total; c0 += CE) {
+        if (c0 + CE < total) load_chunk(c0 + CE, wb);  // static weights: requested ahead
+        const int c1 = min(c0 + CE, total);
+        const int r1 = min(c1, nact);
+        if constexpr (HLDS) {
+#pragma unroll
+            for (int ce = 0; ce < CE; ++ce) {
+                const int ent = c0 + ce;
+                if (ent < nact) {
+                    const int off = uni(ldi(a.act_off + ent)), T = uni(ldi(a.act_off + ent + 1)) - off;
+                    for (int j = 0; j < T; ++j) {
+                        const int p = uni(ldi(a.perm + off + j));
+                        down_accum<LPR, NQ, RP>(wa[ce], s_h + (size_t)(off + j) * I, ldf(a.topk_w + p), p / k, wave,
+                                                lane, s_acc);
+                    }
+                } else if (ent < total) {
+                    const int v = ent - nact;
+                    const float* hs = s_h + hs_off;
+                    for (int t = 0; t < B; ++t)
+                        down_accum<LPR, NQ, RP>(wa[ce], hs + (size_t)t * a.Is + (size_t)v * I, 1.0f, t, wave,
+                                                lane, s_acc);
+                }
+            }
+        } else {
+            // routed entries of the chunk: their h rows are consecutive slots
+            if (c0 < r1) {
+                const int sa = uni(ldi(a.act_off + c0)), sb = uni(ldi(a.act_off + r1));
+                for (int b0 = sa; b0 < sb; b0 += PB) {
+                    const int b1 = min(sb, b0 + PB);
+                    stage_rows(a.h, I, b0, b1);
+                    __syncthreads();
+#pragma unroll
+                    for (int ce = 0; ce < CE; ++ce) {
+                        const int ent = c0 + ce;
+                        if (ent < r1) {
+                            const int o0 = max(uni(ldi(a.act_off + ent)), b0);
+                            const int o1 = min(uni(ldi(a.act_off + ent + 1)), b1);
+                            for (int sl = o0; sl < o1; ++sl) {
+                                const int p = uni(ldi(a.perm + sl));
+                                down_accum<LPR, NQ, RP>(wa[ce], s_h + (size_t)(sl - b0) * I, ldf(a.topk_w + p), p / k,
+                                                        wave, lane, s_acc);
+                            }
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+            // shared-expert column blocks of the chunk: all B tokens each
+#pragma unroll
+            for (int ce = 0; ce < CE; ++ce) {
+                const int ent = c0 + ce;
+                if (ent >= nact && ent < c1) {
+                    const int v = ent - nact;
+                    for (int t0 = 0; t0 < B; t0 += PB) {
+                        const int t1 = min(B, t0 + PB);
+                        stage_rows(a.hs + (size_t)v * I, a.Is, t0, t1);
+                        __syncthreads();
+                        for (int t = t0; t < t1; ++t)
+                            down_accum<LPR, NQ, RP>(wa[ce], s_h + (size_t)(t - t0) * I, 1.0f, t, wave, lane, s_acc);
+                        __syncthreads();
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int ce = 0; ce < CE; ++ce)
+#pragma unroll
+            for (int rp = 0; rp < RP; ++rp)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) wa[ce][rp][q] = wb[ce][rp][q];
+    }
+    // the lane that accumulated (t, row) also writes it: no barrier needed
+    if (c == LPR - 1) {
+#pragma unroll
+        for (int rp = 0; rp < RP; ++rp) {
+            const int rl = (rp * 4 + wave) * RW + rw;
+            const int r = row0 + rl;
+            for (int t = 0; t < B; ++t) {
+                float v = s_acc[t * R + rl];
+                if (mode == DOWN_SHARED) {
+                    st_dev(a.s_out + (size_t)t * H + r, v);
+                    continue;
+                }
+                if (mode == DOWN_ROUTED && a.s_out) v += ld_dev(a.s_out + (size_t)t * H + r);
+                if (a.add_residual) v += __uint_as_float((uint32_t)a.x[(size_t)t * H + r] << 16);
+                a.out[(size_t)t * H + r] = f32_to_bf16_rne(v);
+            }
+        }
+    }
+}
+
+
+}  // namespace moe

@@ -67,6 +67,9 @@ def test_supported_configs_plan(kw):
     (dict(force_variant=3), moe.MOE_ERR_INVALID),
     (dict(mfma_min_tokens=-1), moe.MOE_ERR_INVALID),
     (dict(shared_stream=2), moe.MOE_ERR_INVALID),
+    (dict(topk_launch=3), moe.MOE_ERR_INVALID),
+    (dict(single_launch=3), moe.MOE_ERR_INVALID),
+    (dict(single_launch=-1), moe.MOE_ERR_INVALID),
     (dict(batch=64, force_variant=moe.VARIANT_SMALL_M), moe.MOE_ERR_UNSUPPORTED),
     (dict(router_bias=0x1002), moe.MOE_ERR_INVALID),
     (dict(hidden=7160), moe.MOE_ERR_UNSUPPORTED),
@@ -119,7 +122,9 @@ def test_auto_variant(batch, variant):
     assert info.variant == variant
     # front (router + shared gate/up), [top-k], routed gate/up, down
     assert info.router_mfma == (1 if batch > 4 else 0)
+    assert info.single_launch == 0
     assert info.n_kernels == 3 + info.router_mfma
+    assert info.layer_grid == 0
     assert info.shared_stream == 0
     assert info.workspace_bytes > 0
     if variant == moe.VARIANT_SPLIT_K:
@@ -130,6 +135,37 @@ def test_auto_variant(batch, variant):
     p.destroy()
     p = moe.Plan(cfg(batch=batch, shared_stream=1))
     assert p.info().n_kernels == 4 + (1 if batch > 4 else 0) and p.info().shared_stream == 1
+    assert p.info().single_launch == 0
+    p.destroy()
+    p = moe.Plan(cfg(batch=batch, single_launch=moe.SINGLE_OFF))
+    assert p.info().n_kernels == 3 + (1 if batch > 4 else 0) and p.info().single_launch == 0
+    p.destroy()
+    if batch <= 4:
+        p = moe.Plan(cfg(batch=batch, single_launch=moe.SINGLE_REQUIRED))
+        assert p.info().n_kernels == 1 and p.info().single_launch == 1
+        assert p.info().layer_grid == 0  # set by the first forward
+        p.destroy()
+
+
+@pytest.mark.parametrize("kw,fused", [
+    (dict(), 1), (dict(batch=4), 1), (dict(batch=5), 0),
+    (dict(hidden=256, n_experts=8, top_k=2, inter=128, shared_inter=128, score_fn=moe.SOFTMAX), 1),
+    (dict(shared_inter=0), 1), (dict(inter=64, shared_inter=64), 1), (dict(inter=512, shared_inter=512), 1),
+    (dict(inter=1536, shared_inter=1536, top_k=2), 1), (dict(inter=2560, shared_inter=0, top_k=1), 0),
+    (dict(inter=2048, shared_inter=2048), 0),                  # h rows exceed the LDS budget
+    (dict(hidden=16384, batch=4), 0),                          # activations exceed it
+    (dict(topk_launch=2), 0), (dict(shared_stream=1), 0),
+])
+def test_single_launch_policy(kw, fused):
+    p = moe.Plan(cfg(**kw))
+    assert p.info().single_launch == 0  # never the default
+    p.destroy()
+    st = plan_status(cfg(single_launch=moe.SINGLE_REQUIRED, **kw))
+    assert st == (moe.MOE_OK if fused else moe.MOE_ERR_UNSUPPORTED)
+    if not fused:
+        assert "single_launch" in moe.last_error()
+    p = moe.Plan(cfg(single_launch=moe.SINGLE_OFF, **kw))
+    assert p.info().single_launch == 0
     p.destroy()
 
 
@@ -154,7 +190,7 @@ def test_profiling_toggle_without_device():
     p = moe.Plan(cfg())
     p.set_profiling(True)
     prof = p.profile_read()
-    assert set(prof) == {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine"}
+    assert set(prof) == {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine", "layer"}
     assert all(v == (0.0, 0) for v in prof.values())
     p.set_profiling(False)
     p.destroy()

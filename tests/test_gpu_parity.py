@@ -49,6 +49,13 @@ def test_tiny(tiny, batch, resid):
     check(tiny, shape, batch, "tiny B=%d resid=%d" % (batch, resid))
 
 
+@pytest.mark.parametrize("batch", [1, 2, 3, 4])
+def test_tiny_single_launch(tiny, batch):
+    shape = shape_of(synthetic.TINY)
+    m, st, info = check(tiny, shape, batch, "tiny single B=%d" % batch, single_launch=moe.SINGLE_REQUIRED)
+    assert info.single_launch == 1
+
+
 @pytest.mark.parametrize("batch,kw", [
     (8, dict(force_variant=moe.VARIANT_SMALL_M)),
     (64, dict(force_variant=moe.VARIANT_SMALL_M)),
@@ -71,11 +78,82 @@ def tp8():
     return DeviceLayer(synthetic.TP8)
 
 
-@pytest.mark.parametrize("batch", [1, 2, 3, 8, 16, 64])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 8, 16, 64])
 def test_tp8_uniform(tp8, batch):
     shape = shape_of(synthetic.TP8)
     m, st, info = check(tp8, shape, batch, "tp8 B=%d" % batch)
     assert info.variant == (moe.VARIANT_SMALL_M if batch <= 2 else moe.VARIANT_SPLIT_K)
+    assert info.single_launch == 0
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 4])
+def test_tp8_single_launch(tp8, batch):
+    shape = shape_of(synthetic.TP8)
+    m, st, info = check(tp8, shape, batch, "tp8 single B=%d" % batch, single_launch=moe.SINGLE_REQUIRED)
+    assert info.single_launch == 1 and info.n_kernels == 1 and 0 < info.layer_grid
+
+
+@pytest.mark.parametrize("batch,kw", [
+    (1, dict(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=1)),  # MFMA tiles inside the single launch
+    (3, dict(force_variant=moe.VARIANT_SMALL_M)),
+    (4, dict(mfma_min_tokens=2)),
+])
+def test_tp8_single_launch_variants(tp8, batch, kw):
+    shape = shape_of(synthetic.TP8)
+    m, st, info = check(tp8, shape, batch, "tp8 single B=%d %s" % (batch, kw),
+                        single_launch=moe.SINGLE_REQUIRED, **kw)
+    assert info.single_launch == 1
+    if kw.get("mfma_min_tokens") == 1:
+        assert st.mfma_tiles > 0 and st.gemv_tiles == 0
+
+
+@pytest.mark.parametrize("B", [1, 2, 3])
+def test_single_launch_bitwise_equals_staged(tp8, B):
+    """At batch <= 3 of the TP8 shape every stage is deterministic (GEMV tiles,
+    one shared column block), and the single launch does the same arithmetic
+    in the same order as the staged launches: the outputs must be identical
+    bit for bit, on every one of many forwards with fresh inputs.  A hand-off
+    that read stale data (a previous forward's h, routing or logits) would
+    break this."""
+    shape = shape_of(synthetic.TP8)
+    fused = make_plan(tp8, shape, B, single_launch=moe.SINGLE_REQUIRED)
+    staged = make_plan(tp8, shape, B, single_launch=moe.SINGLE_OFF)
+    g = torch.Generator().manual_seed(1234 + B)
+    for it in range(40):
+        x = (torch.randn(B, shape.hidden, generator=g) * (1 + it % 3)).to(torch.bfloat16).cuda()
+        o1 = torch.empty_like(x)
+        o2 = torch.empty_like(x)
+        fused.forward(x, tp8.router_w, tp8.expert_w, tp8.shared_w, o1)
+        staged.forward(x, tp8.router_w, tp8.expert_w, tp8.shared_w, o2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "forward %d differs" % it
+    assert fused.stats().error_flags == 0 and staged.stats().error_flags == 0
+    fused.destroy()
+    staged.destroy()
+
+
+def test_single_launch_repeated_forwards(tp8):
+    """The single launch re-arms its counters at exit: many forwards in a row
+    on one plan (graph replays, then eager profiled launches) stay correct."""
+    shape = shape_of(synthetic.TP8)
+    for B in (1, 4):
+        plan = make_plan(tp8, shape, B, single_launch=moe.SINGLE_REQUIRED)
+        assert plan.info().single_launch == 1
+        x, _ = gap_x(tp8, shape, B, offset=900 + B)
+        ref = run_oracle(tp8, shape, x)
+        for it in range(20):
+            out, idx, w, nu = run_gpu(plan, tp8, x, shape)
+            if it % 5 == 0:
+                compare(out, idx, w, *ref, label="repeat B=%d it %d" % (B, it))
+        compare_out(out, ref[0], "repeat B=%d last" % B)
+        plan.set_profiling(True)
+        for it in range(5):
+            out, idx, w, nu = run_gpu(plan, tp8, x, shape)
+        prof = plan.profile_read()
+        assert {k for k, v in prof.items() if v[1]} == {"layer"}
+        compare(out, idx, w, *ref, label="profiled B=%d" % B)
+        assert plan.stats().error_flags == 0
+        plan.destroy()
 
 
 def test_tp8_moe_only(tp8):
@@ -104,17 +182,19 @@ def test_tp8_zipf_skew(tp8_zipf):
     assert st.n_unique < 200
 
 
-def test_tp8_identical_tokens_route_together(tp8):
+@pytest.mark.parametrize("B,single", [(4, 0), (4, 2), (16, 0)])
+def test_tp8_identical_tokens_route_together(tp8, B, single):
     """Every token identical: the k selected experts each get all B tokens, so
-    the routed experts go through the split-K MFMA tiles."""
+    the routed experts go through the split-K MFMA tiles (inside the single
+    launch at B = 4)."""
     shape = shape_of(synthetic.TP8)
-    B = 16
     x1, _ = gap_x(tp8, shape, 1, offset=500)
     x = np.repeat(x1, B, axis=0)
-    plan = make_plan(tp8, shape, B)
+    plan = make_plan(tp8, shape, B, single_launch=single)
     out, idx, w, nu = run_gpu(plan, tp8, x, shape)
     out64, idx_o, w_o = run_oracle(tp8, shape, x)
     compare(out, idx, w, out64, idx_o, w_o, "identical tokens")
+    assert plan.info().single_launch == (1 if single else 0)
     st = plan.stats()
     assert nu == 8 and st.mfma_tiles > 0 and st.gemv_tiles == 0
     plan.destroy()
@@ -234,3 +314,12 @@ def test_edge_shapes(case):
     shape = shape_of(wl, renormalize=ren, routed_scale=scale)
     for b in sorted({1, B}):
         check(layer, shape, b, "%s B=%d" % (name, b))
+    # the single launch, where the shape allows it
+    for b in sorted({1, min(B, 4)}):
+        try:
+            make_plan(layer, shape, b, single_launch=moe.SINGLE_REQUIRED).destroy()
+        except moe.MoeError as e:
+            assert e.status == moe.MOE_ERR_UNSUPPORTED
+            continue
+        m, st, info = check(layer, shape, b, "%s single B=%d" % (name, b), single_launch=moe.SINGLE_REQUIRED)
+        assert info.single_launch == 1
