@@ -86,7 +86,8 @@ struct GateUpArgs {
     int32_t kslice;             // K elements per split (multiple of 32)
 };
 
-// Down projection + routing-weighted combine + shared expert + residual.
+// Down projection + routing-weighted combine + shared expert + residual,
+// output-stationary (the single launch's down tasks, rows x all entries).
 struct DownArgs {
     const uint16_t* x;       // bf16 [B][H] (residual)
     const uint16_t* w2;      // bf16 [E][H][I]
@@ -104,6 +105,36 @@ struct DownArgs {
     int32_t add_residual;
     int32_t n_experts;
     int32_t h_in_lds;        // 1: all of h and hs are staged in LDS at kernel start
+};
+
+// Down projection, expert-major (staged launches, larger batches): one
+// workgroup per (entry, block of 256 output rows), entries = active routed
+// experts then the shared expert's Is/I column blocks.  Each writes fp32
+// partial rows per pair (or per shared block and token); combine_kernel then
+// sums them in a fixed order (routing weights, shared blocks, residual) into
+// bf16.
+struct DownXArgs {
+    const uint16_t* x;       // bf16 [B][H] (residual)
+    const uint16_t* w2;      // bf16 [E][H][I]
+    const uint16_t* s2;      // bf16 [H][Is] or null
+    const int32_t* n_act;
+    const int32_t* act_e;
+    const int32_t* act_off;
+    const int32_t* perm;     // slot -> pair id
+    const float* topk_w;     // [B][k]
+    const float* h;          // fp32 [B*k][I] routed h, slot-major
+    const float* hs;         // fp32 [B][Is] shared h
+    float* part;             // fp32 [B*k][H] per-pair partial outputs
+    float* part_s;           // fp32 [nsh][B][H] per-shared-block partial outputs
+    int32_t* meta;
+    uint16_t* out;           // bf16 [B][H]
+    int32_t H, I, Is, B, k;
+    int32_t add_residual;
+    int32_t n_experts;
+    int32_t max_act;         // routed entries of the grid
+    int32_t nsh;             // shared column blocks (Is / I, 0 without a shared expert)
+    int32_t mfma_min_tokens; // entries with at least this many tokens use MFMA (0: never)
+    int32_t gemv_max_tokens; // GEMV tiles stage at most this many tokens' h in LDS
 };
 
 // First launch of a layer: the router (GEMV for batch <= 4, split-K MFMA
@@ -158,6 +189,11 @@ KernelPick pick_front(const FrontArgs& f, bool small_router, bool select_in_rout
 int front_router_blocks(const RouterArgs& a, bool small_router);
 KernelPick pick_topk(const RouterArgs& a);
 KernelPick pick_gateup(const GateUpArgs& a, int max_entries, int gemv_tokens);
+constexpr int kDownXRows = 256;           // output rows per expert-major down tile
+constexpr int kDownXLds = 32 * 1024;      // LDS for a GEMV tile's staged h rows
+KernelPick pick_down_x(const DownXArgs& a);
+KernelPick pick_combine(const DownXArgs& a);
+// Output-stationary down (down_rows over all entries) for small batches.
 KernelPick pick_down(const DownArgs& a);
 // Single-launch layer; func is null when the shape has no instantiation.
 KernelPick pick_layer(const LayerArgs& L, size_t lds_bytes);

@@ -58,18 +58,20 @@ constexpr int kMaxProfiledForwards = 1024;
 constexpr int kSmallRouterMaxBatch = 4;
 constexpr size_t kSmallRouterLds = 56 * 1024;
 
-constexpr size_t kDownHLds = 48 * 1024;
-constexpr size_t kLayerLds = 56 * 1024;  // dynamic LDS of the single launch: x staging, then h rows
+constexpr size_t kLayerLds = 56 * 1024;
+constexpr size_t kDownHLds = 48 * 1024;   // output-stationary down: h fully staged in LDS up to this
+constexpr int kDownOsMaxBatch = 4;        // output-stationary down up to this batch, expert-major above  // dynamic LDS of the single launch: x staging, then h rows
 
-enum Slot { S_FRONT = 0, S_TOPK = 1, S_GATEUP = 2, S_SHARED = 3, S_DOWN = 4, S_LAYER = 5, S_COUNT = 6 };
+enum Slot { S_FRONT = 0, S_TOPK = 1, S_GATEUP = 2, S_SHARED = 3, S_DOWN = 4, S_LAYER = 5, S_COMBINE = 6,
+            S_COUNT = 7 };
 const char* kSlotNames[S_COUNT] = {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine",
-                                   "layer"};
+                                   "layer", "combine"};
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
     size_t meta, z, zacc, topk_idx, topk_w, act_e, act_off, perm, sh_act_e, sh_act_off, sh_perm;
-    size_t h, hs, g_acc, g_acc_s, tile_cnt, tile_cnt_s, s_out, total;
+    size_t h, hs, g_acc, g_acc_s, tile_cnt, tile_cnt_s, s_out, part, part_s, total;
 };
 
 }  // namespace
@@ -86,6 +88,7 @@ struct moe_decode_plan_s {
     bool shared_stream;   // shared gate/up on the second stream instead of the front launch
     bool select_in_router;// batch <= 4: top-k + bucketing in the router's last workgroup
     bool fused;           // the whole layer as one persistent launch
+    bool expert_major;    // staged down: expert-major tiles + combine launch (else output-stationary)
     size_t layer_lds;     // its dynamic LDS bytes
     int layer_grid = 0;   // its workgroups (set on the first forward)
     Layout L;
@@ -102,15 +105,16 @@ struct moe_decode_plan_s {
     RouterArgs& ra = fa.r;
     GateUpArgs& gs = fa.s;
     GateUpArgs ga{};
-    DownArgs da{};
+    DownArgs da{};     // down of the single launch
+    DownXArgs dx{};    // down of the staged launches
     LayerArgs la{};
-    KernelPick kf{}, kt{}, kg{}, ks{}, kd{}, kl{};
+    KernelPick kf{}, kt{}, kg{}, ks{}, kd{}, kl{}, kc{};
 
     // graph
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     hipGraphNode_t n_front = nullptr, n_topk = nullptr, n_gateup = nullptr, n_shared = nullptr,
-                   n_down = nullptr, n_layer = nullptr;
+                   n_down = nullptr, n_layer = nullptr, n_combine = nullptr;
     const void* args_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // in the arg blocks
     const void* graph_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};  // in the graph exec
     bool have_forward = false;
@@ -168,7 +172,7 @@ moe_status validate(const moe_decode_config* c) {
     return MOE_OK;
 }
 
-Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fused) {
+Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fused, bool expert_major) {
     const size_t B = c.batch, E = c.n_experts, k = c.top_k, I = c.inter, Is = c.shared_inter;
     Layout L{};
     size_t o = 0;
@@ -197,6 +201,10 @@ Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fus
         L.tile_cnt_s = take((Is / kPairsPerMfmaTile + 1) * 4);
     }
     if (fused && Is) L.s_out = take(B * c.hidden * 4);
+    if (expert_major) {  // per-pair / per-shared-block partials of the expert-major down
+        L.part = take(B * k * c.hidden * 4);
+        L.part_s = take((Is / I) * B * c.hidden * 4 + 4);
+    }
     L.total = o;
     return L;
 }
@@ -280,7 +288,6 @@ void fill_static_args(moe_decode_plan_s* p) {
                               ? c.shared_inter / kPairsPerGemvTile : 0;
 
     DownArgs& d = p->da;
-    d.h_in_lds = down_h_lds_bytes(c.batch, c.top_k, c.inter, c.shared_inter) <= kDownHLds ? 1 : 0;
     d.n_act = g.n_act;
     d.act_e = r.act_e;
     d.act_off = r.act_off;
@@ -295,7 +302,31 @@ void fill_static_args(moe_decode_plan_s* p) {
     d.k = c.top_k;
     d.add_residual = c.add_residual;
     d.n_experts = c.n_experts;
+    d.h_in_lds = down_h_lds_bytes(c.batch, c.top_k, c.inter, c.shared_inter) <= kDownHLds ? 1 : 0;
     d.s_out = (p->fused && has_shared(p)) ? at<float>(p, p->L.s_out) : nullptr;
+
+    DownXArgs& x = p->dx;
+    x.n_act = g.n_act;
+    x.act_e = r.act_e;
+    x.act_off = r.act_off;
+    x.perm = r.perm;
+    x.topk_w = r.topk_w;
+    x.h = g.h;
+    x.hs = d.hs;
+    x.part = p->expert_major ? at<float>(p, p->L.part) : nullptr;
+    x.part_s = p->expert_major ? at<float>(p, p->L.part_s) : nullptr;
+    x.meta = r.meta;
+    x.H = c.hidden;
+    x.I = c.inter;
+    x.Is = c.shared_inter;
+    x.B = c.batch;
+    x.k = c.top_k;
+    x.add_residual = c.add_residual;
+    x.n_experts = c.n_experts;
+    x.max_act = p->max_act;
+    x.nsh = c.shared_inter / c.inter;
+    x.mfma_min_tokens = p->mfma_min;
+    x.gemv_max_tokens = std::min(32, kDownXLds / (4 * c.inter));
 
     if (p->fused) {
         LayerArgs& l = p->la;
@@ -330,11 +361,20 @@ void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, con
     p->da.w2 = ew + (size_t)c.n_experts * 2 * c.inter * c.hidden;
     p->da.s2 = has_shared(p) ? sw + (size_t)2 * c.shared_inter * c.hidden : nullptr;
     p->da.out = static_cast<uint16_t*>(out);
+    p->dx.x = xb;
+    p->dx.w2 = p->da.w2;
+    p->dx.s2 = p->da.s2;
+    p->dx.out = p->da.out;
     p->kf = pick_front(p->fa, p->small_router, p->select_in_router, p->shared_mfma ? 0 : c.batch);
     if (!p->select_in_router) p->kt = pick_topk(p->ra);
     p->kg = pick_gateup(p->ga, p->max_act, p->routed_gemv_tb);
     if (has_shared(p) && p->shared_stream) p->ks = pick_gateup(p->gs, 1, p->shared_mfma ? 1 : c.batch);
-    p->kd = pick_down(p->da);
+    if (p->expert_major) {
+        p->kd = pick_down_x(p->dx);
+        p->kc = pick_combine(p->dx);
+    } else {
+        p->kd = pick_down(p->da);
+    }
     if (p->fused) {
         p->la.f = p->fa;
         p->la.g = p->ga;
@@ -427,8 +467,13 @@ moe_status enqueue_eager(moe_decode_plan_s* p, hipStream_t stream, hipEvent_t* e
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_GATEUP + 1], stream));
     if (side) HIP_TRY(hipStreamWaitEvent(stream, p->ev_join, 0));
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_DOWN], stream));
-    if ((st = launch(p->kd, &p->da, stream))) return st;
+    if ((st = launch(p->kd, p->expert_major ? (void*)&p->dx : (void*)&p->da, stream))) return st;
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_DOWN + 1], stream));
+    if (p->expert_major) {
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_COMBINE], stream));
+        if ((st = launch(p->kc, &p->dx, stream))) return st;
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_COMBINE + 1], stream));
+    }
     return MOE_OK;
 }
 
@@ -456,7 +501,8 @@ moe_status build_graph(moe_decode_plan_s* p) {
     void* ar[] = {&p->ra};
     void* ag[] = {&p->ga};
     void* as[] = {&p->gs};
-    void* ad[] = {&p->da};
+    void* ad[] = {p->expert_major ? (void*)&p->dx : (void*)&p->da};
+    void* ac[] = {&p->dx};
     hipKernelNodeParams np = node_params(p->kf, af);
     HIP_TRY(hipGraphAddKernelNode(&p->n_front, p->graph, nullptr, 0, &np));
     hipGraphNode_t route_done = p->n_front;
@@ -476,6 +522,10 @@ moe_status build_graph(moe_decode_plan_s* p) {
     }
     np = node_params(p->kd, ad);
     HIP_TRY(hipGraphAddKernelNode(&p->n_down, p->graph, deps, ndeps, &np));
+    if (p->expert_major) {
+        np = node_params(p->kc, ac);
+        HIP_TRY(hipGraphAddKernelNode(&p->n_combine, p->graph, &p->n_down, 1, &np));
+    }
     HIP_TRY(hipGraphInstantiate(&p->exec, p->graph, nullptr, nullptr, 0));
     return MOE_OK;
 }
@@ -491,7 +541,8 @@ moe_status patch_graph(moe_decode_plan_s* p) {
     void* ar[] = {&p->ra};
     void* ag[] = {&p->ga};
     void* as[] = {&p->gs};
-    void* ad[] = {&p->da};
+    void* ad[] = {p->expert_major ? (void*)&p->dx : (void*)&p->da};
+    void* ac[] = {&p->dx};
     hipKernelNodeParams np = node_params(p->kf, af);
     HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_front, &np));
     if (!p->select_in_router) {
@@ -506,6 +557,10 @@ moe_status patch_graph(moe_decode_plan_s* p) {
     }
     np = node_params(p->kd, ad);
     HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_down, &np));
+    if (p->expert_major) {
+        np = node_params(p->kc, ac);
+        HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_combine, &np));
+    }
     return MOE_OK;
 }
 
@@ -584,7 +639,8 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
             return fail(MOE_ERR_UNSUPPORTED, "single_launch = 2: %s", why);
         }
     }
-    p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K, p->fused);
+    p->expert_major = c.batch > kDownOsMaxBatch;
+    p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K, p->fused, p->expert_major);
     *out_plan = p;
     return MOE_OK;
 }
@@ -680,7 +736,9 @@ moe_status moe_decode_plan_info(moe_decode_plan_t p, moe_decode_info* info) {
     g_err.clear();
     if (!p || !info) return fail(MOE_ERR_INVALID, "NULL argument");
     info->variant = p->variant;
-    info->n_kernels = p->fused ? 1 : 3 + (p->select_in_router ? 0 : 1) + (has_shared(p) && p->shared_stream ? 1 : 0);
+    info->n_kernels = p->fused ? 1
+                      : 3 + (p->select_in_router ? 0 : 1) + (has_shared(p) && p->shared_stream ? 1 : 0) +
+                            (p->expert_major ? 1 : 0);
     info->mfma_min_tokens = p->mfma_min;
     info->shared_mfma = p->shared_mfma ? 1 : 0;
     info->shared_stream = p->shared_stream ? 1 : 0;
@@ -720,7 +778,8 @@ moe_status moe_decode_profile_read(moe_decode_plan_t p, int32_t cap, double* tot
         for (int s = 0; s < S_COUNT && s < cap; ++s) {
             const bool used = p->fused ? s == S_LAYER
                               : !((s == S_SHARED && !(has_shared(p) && p->shared_stream)) ||
-                                  (s == S_TOPK && p->select_in_router) || s == S_LAYER);
+                                  (s == S_TOPK && p->select_in_router) || s == S_LAYER ||
+                                  (s == S_COMBINE && !p->expert_major));
             if (!used) continue;
             hipEvent_t a = p->prof_events[((size_t)f * S_COUNT + s) * 2];
             hipEvent_t b = p->prof_events[((size_t)f * S_COUNT + s) * 2 + 1];

@@ -871,8 +871,11 @@ __device__ __forceinline__ void down_rows(const DownArgs& a, int row_block, floa
         }
     };
 
-    u32x4 wa[CE][RP][NQ], wb[CE][RP][NQ];
-    load_chunk(0, wa);
+    // two chunk buffers used alternately (the chunk loop is unrolled by two),
+    // so the next chunk's weights are in flight while this one is used and no
+    // register copies force an early wait
+    u32x4 wbuf0[CE][RP][NQ], wbuf1[CE][RP][NQ];
+    load_chunk(0, wbuf0);
     for (int i = tid; i < B * R; i += 256) s_acc[i] = 0.0f;
     wait();
     // LDS layout when HLDS: routed h rows [B*k][I], then shared rows [B][Is]
@@ -896,8 +899,7 @@ __device__ __forceinline__ void down_rows(const DownArgs& a, int row_block, floa
     };
     const int PB = (kDownHStage / 4) / I;  // h rows per staged batch
 
-    for (int c0 = 0; c0 < total; c0 += CE) {
-        if (c0 + CE < total) load_chunk(c0 + CE, wb);  // static weights: requested ahead
+    auto process = [&](int c0, const u32x4 (&wa)[CE][RP][NQ]) {
         const int c1 = min(c0 + CE, total);
         const int r1 = min(c1, nact);
         if constexpr (HLDS) {
@@ -960,12 +962,13 @@ __device__ __forceinline__ void down_rows(const DownArgs& a, int row_block, floa
                 }
             }
         }
-#pragma unroll
-        for (int ce = 0; ce < CE; ++ce)
-#pragma unroll
-            for (int rp = 0; rp < RP; ++rp)
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) wa[ce][rp][q] = wb[ce][rp][q];
+    };
+    for (int c0 = 0; c0 < total; c0 += 2 * CE) {
+        if (c0 + CE < total) load_chunk(c0 + CE, wbuf1);  // static weights: requested ahead
+        process(c0, wbuf0);
+        if (c0 + CE >= total) break;
+        if (c0 + 2 * CE < total) load_chunk(c0 + 2 * CE, wbuf0);
+        process(c0 + CE, wbuf1);
     }
     // the lane that accumulated (t, row) also writes it: no barrier needed
     if (c == LPR - 1) {

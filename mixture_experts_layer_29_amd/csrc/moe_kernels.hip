@@ -139,11 +139,250 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// down, output-stationary (staged launches, small batches): each workgroup
+// owns a block of output rows and runs every active expert and shared column
+// block over them (down_rows), so the combine needs no second pass
+// ---------------------------------------------------------------------------
+
 template <int LPR, int NQ, int RP, bool HLDS>
 __global__ __launch_bounds__(256) void down_combine_kernel(DownArgs a) {
     extern __shared__ __align__(16) float s_h[];
     __shared__ float s_acc[kMaxBatch * DownShape<LPR, NQ, RP>::R];
     down_rows<LPR, NQ, RP, HLDS, DOWN_ALL>(a, blockIdx.x, s_h, s_acc, [] {});
+}
+
+// ---------------------------------------------------------------------------
+// down, expert-major (staged launches, larger batches)
+// ---------------------------------------------------------------------------
+
+// Packs 8 floats into bf16 hi and lo parts (v ~= hi + lo to ~2^-16 relative):
+// the MFMA down tile multiplies W2 by both, which keeps h at near-fp32
+// precision through a bf16 matrix core.
+__device__ __forceinline__ void split_bf16x8(const float4 f0, const float4 f1, u32x4& hi, u32x4& lo) {
+    const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h[i] = f32_to_bf16_rne(v[i]);
+        l[i] = f32_to_bf16_rne(v[i] - __uint_as_float(h[i] << 16));
+    }
+    hi = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    lo = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+}
+
+// One workgroup: output rows [r0, r0 + kDownXRows) of one entry (a routed
+// expert with T tokens, or a shared column block with all B tokens); wave w
+// owns the 64-row band r0 + 64w.  Token j's h row is hsrc + j * hstride (I
+// floats); its partial output row is dst + s_dsto[j] (H floats).
+//  GEMV (T <= gemv_max_tokens, no MFMA): h staged in LDS; LPR lanes per row,
+//    NQ 16-byte units per lane per row; the band's rows are loaded in batches
+//    of 16 units per lane, the next batch requested before the current one is
+//    used.
+//  MFMA (else): per 32-column step, each wave multiplies its four 16-row
+//    groups (A = W2 rows) by h^T (B, split into bf16 hi + lo, loaded once per
+//    step for all four groups) with mfma_f32_16x16x32_bf16.
+// The partials are combined by combine_kernel, the next launch.
+template <int LPR, int NQ>
+__global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
+    extern __shared__ __align__(16) float s_h[];  // [T][I] (GEMV tiles)
+    __shared__ int s_dsto[kMaxBatch];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H, I = a.I, B = a.B, k = a.k;
+    const int nrb = (H + kDownXRows - 1) / kDownXRows;
+    const int rb = blockIdx.x % nrb, ent = blockIdx.x / nrb;
+    const int r0 = rb * kDownXRows;
+    const int band = r0 + 64 * wave;
+    const bool band_ok = band < H;  // H is a multiple of 64
+    const int nact = uni(*a.n_act);
+
+    const uint16_t* W;
+    const float* hsrc;
+    float* dst;
+    int ld, hstride, T;
+    if (ent < a.max_act) {
+        if (ent >= nact) {
+            return;
+        }
+        int e = uni(a.act_e[ent]);
+        const int off = uni(a.act_off[ent]);
+        T = uni(a.act_off[ent + 1]) - off;
+        if ((unsigned)e >= (unsigned)a.n_experts || off < 0 || T < 1 || off + T > B * k || T > kMaxBatch) {
+            if (tid == 0 && rb == 0) atomicOr(&a.meta[M_ERR], ERR_TILE);
+            return;
+        }
+        W = a.w2 + (size_t)e * H * I;
+        ld = I;
+        hsrc = a.h + (size_t)(T ? off : 0) * I;
+        hstride = I;
+        dst = a.part;
+        if (tid < T) s_dsto[tid] = a.perm[off + tid] * H;
+    } else {
+        const int v = ent - a.max_act;
+        W = a.s2 + (size_t)v * I;
+        ld = a.Is;
+        hsrc = a.hs + (size_t)v * I;
+        hstride = a.Is;
+        T = B;
+        dst = a.part_s;
+        if (tid < B) s_dsto[tid] = (v * B + tid) * H;
+    }
+    const bool mfma = (a.mfma_min_tokens > 0 && T >= a.mfma_min_tokens) || T > a.gemv_max_tokens;
+    const u32x4 zero = u32x4{0, 0, 0, 0};
+
+    if (T > 0 && !mfma) {
+        constexpr int RW = 64 / LPR, P = 64 / RW;            // rows per pass, passes per band
+        constexpr int QB = (16 / NQ) < P ? 16 / NQ : P;      // passes per batch of loads
+        const int rw = lane / LPR, c = lane % LPR;
+        auto load = [&](int q0, u32x4 (&w)[QB][NQ]) {
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                const int row = band + (q0 + q) * RW + rw;
+                const bool ok = band_ok && q0 + q < P;
+#pragma unroll
+                for (int u = 0; u < NQ; ++u)
+                    w[q][u] = ok ? ld16(W + (size_t)row * ld + 8 * (c + LPR * u)) : zero;
+            }
+        };
+        // two register buffers; the batch loop is unrolled, so they alternate
+        // without copies and each batch's loads are waited for only when used
+        u32x4 wbuf[2][QB][NQ];
+        load(0, wbuf[0]);
+        {   // stage h while the first batch of weights is in flight
+            const int I4 = I / 4;
+            float4* d = reinterpret_cast<float4*>(s_h);
+            for (int i = tid; i < T * I4; i += 256) {
+                const int j = i / I4, c4 = i - j * I4;
+                d[i] = *reinterpret_cast<const float4*>(hsrc + (size_t)j * hstride + 4 * c4);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int q0 = 0; q0 < P; q0 += QB) {
+            u32x4 (&wa)[QB][NQ] = wbuf[(q0 / QB) & 1];
+            if (q0 + QB < P) load(q0 + QB, wbuf[((q0 / QB) + 1) & 1]);
+            if (band_ok) {
+#pragma unroll
+                for (int q = 0; q < QB; ++q) {
+                    if (q0 + q < P) {
+                        const int row = band + (q0 + q) * RW + rw;
+                        for (int j = 0; j < T; ++j) {
+                            float acc = 0.0f;
+#pragma unroll
+                            for (int u = 0; u < NQ; ++u) {
+                                const float4* hp =
+                                    reinterpret_cast<const float4*>(s_h + (size_t)j * I + 8 * (c + LPR * u));
+                                acc = dot8_f32(wa[q][u], hp[0], hp[1], acc);
+                            }
+                            acc = group_sum<LPR>(acc);
+                            if (c == LPR - 1) dst[s_dsto[j] + row] = acc;
+                        }
+                    }
+                }
+            }
+        }
+    } else if (T > 0) {
+        __syncthreads();  // s_dsto
+        const int tl = lane & 15, kq = lane >> 4;
+        const int NT = (T + 15) >> 4;
+        const uint16_t* arow = W + (size_t)(band + tl) * ld + 8 * kq;  // group g: + 16 g rows
+        const float* hrow[4];
+        bool hok[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int j = tt * 16 + tl;
+            hok[tt] = j < T;
+            hrow[tt] = hsrc + (size_t)(hok[tt] ? j : 0) * hstride + 8 * kq;
+        }
+        f32x4 acc[4][4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) acc[g][tt] = f32x4{0, 0, 0, 0};
+        constexpr int nsteps = LPR * NQ / 4;  // I / 32
+#pragma unroll
+        for (int s0 = 0; s0 < nsteps; s0 += 2) {
+            u32x4 A[2][4];
+            float4 X0[2][4], X1[2][4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bool sok = s0 + u < nsteps;
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    A[u][g] = (sok && band_ok) ? ld16(arow + (size_t)16 * g * ld + 32 * (s0 + u)) : zero;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const bool ok = sok && tt < NT && hok[tt];
+                    const float4* hp = reinterpret_cast<const float4*>(hrow[tt] + 32 * (s0 + u));
+                    X0[u][tt] = ok ? hp[0] : float4{0, 0, 0, 0};
+                    X1[u][tt] = ok ? hp[1] : float4{0, 0, 0, 0};
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (s0 + u >= nsteps) break;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    if (tt < NT) {
+                        u32x4 bh, bl;
+                        split_bf16x8(X0[u][tt], X1[u][tt], bh, bl);
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const bf16x8 Aw = __builtin_bit_cast(bf16x8, A[u][g]);
+                            acc[g][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aw, __builtin_bit_cast(bf16x8, bh),
+                                                                                 acc[g][tt], 0, 0, 0);
+                            acc[g][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aw, __builtin_bit_cast(bf16x8, bl),
+                                                                                 acc[g][tt], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+        // D layout: lane holds rows 4*(lane/16)+r of the group, column (token) lane%16
+        if (band_ok) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int j = tt * 16 + tl;
+                if (tt < NT && j < T) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float* dp = dst + s_dsto[j] + band + 16 * g + 4 * kq;
+                        *reinterpret_cast<float4*>(dp) =
+                            float4{acc[g][tt][0], acc[g][tt][1], acc[g][tt][2], acc[g][tt][3]};
+                    }
+                }
+            }
+        }
+    }
+
+}
+
+// out[t][r] = bf16( sum_j w[t][j] * part[t*k+j][r] + sum_sb part_s[sb][t][r] (+ x) ),
+// summed in that fixed order; four rows per thread.
+__global__ __launch_bounds__(256) void combine_kernel(DownXArgs a) {
+    const int H = a.H, k = a.k, B = a.B;
+    const int i4 = blockIdx.x * 256 + threadIdx.x;
+    if (i4 >= B * H / 4) return;
+    const int t = (4 * i4) / H, r = 4 * i4 - t * H;
+    float4 v = float4{0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+        const int p = t * k + j;
+        const float w = a.topk_w[p];
+        const float4 y = *reinterpret_cast<const float4*>(a.part + (size_t)p * H + r);
+        v.x += w * y.x; v.y += w * y.y; v.z += w * y.z; v.w += w * y.w;
+    }
+    for (int sb = 0; sb < a.nsh; ++sb) {
+        const float4 y = *reinterpret_cast<const float4*>(a.part_s + ((size_t)sb * B + t) * H + r);
+        v.x += y.x; v.y += y.y; v.z += y.z; v.w += y.w;
+    }
+    if (a.add_residual) {
+        const uint2 xb = *reinterpret_cast<const uint2*>(a.x + (size_t)t * H + r);
+        v.x += bf16_lo(xb.x); v.y += bf16_hi(xb.x); v.z += bf16_lo(xb.y); v.w += bf16_hi(xb.y);
+    }
+    const uint32_t o0 = f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+    const uint32_t o1 = f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+    *reinterpret_cast<uint2*>(a.out + (size_t)t * H + r) = uint2{o0, o1};
 }
 
 __global__ void init_lists_kernel(InitArgs a) {
@@ -249,7 +488,7 @@ KernelPick pick_gateup(const GateUpArgs& a, int max_entries, int gemv_tokens) {
     return {f, dim3(max_entries * a.tiles_per_expert), dim3(256), (size_t)gemv_tokens * a.H * 2};
 }
 
-// Output rows per down_combine workgroup for intermediate size I (matches pick_down).
+// Output rows per down row block of the single launch for intermediate size I.
 int down_rows_per_block(int I) {
     const int ur = I / 8;
     if (ur == 8) return DownShape<8, 1, 1>::R;
@@ -259,6 +498,8 @@ int down_rows_per_block(int I) {
 }
 
 size_t down_h_lds_bytes(int B, int k, int I, int Is) { return ((size_t)B * k * I + (size_t)B * Is) * 4; }
+
+
 
 KernelPick pick_down(const DownArgs& a) {
     const int ur = a.I / 8;
@@ -286,6 +527,33 @@ KernelPick pick_down(const DownArgs& a) {
     return {f, dim3(a.H / down_rows_per_block(a.I)), dim3(256), lds};
 }
 
+KernelPick pick_combine(const DownXArgs& a) {
+    return {MOE_FN(combine_kernel), dim3((a.B * a.H / 4 + 255) / 256), dim3(256), 0};
+}
+
+KernelPick pick_down_x(const DownXArgs& a) {
+    const int ur = a.I / 8;
+    const void* f;
+#define MOE_DX(LPR, NQ) f = MOE_FN((down_x_kernel<LPR, NQ>));
+    if (ur == 8) MOE_DX(8, 1)
+    else if (ur == 16) MOE_DX(16, 1)
+    else if (ur == 32) MOE_DX(32, 1)
+    else {
+        switch (ur / 64) {
+            case 1: MOE_DX(64, 1) break;
+            case 2: MOE_DX(64, 2) break;
+            case 3: MOE_DX(64, 3) break;
+            case 4: MOE_DX(64, 4) break;
+            case 5: MOE_DX(64, 5) break;
+            case 6: MOE_DX(64, 6) break;
+            case 7: MOE_DX(64, 7) break;
+            default: MOE_DX(64, 8) break;
+        }
+    }
+#undef MOE_DX
+    const int grid = (a.max_act + a.nsh) * ((a.H + kDownXRows - 1) / kDownXRows);
+    return {f, dim3(grid), dim3(256), (size_t)a.gemv_max_tokens * a.I * 4};
+}
 
 template <int TB>
 const void* layer_fn(int ns, int shape);  // moe_layer_tb{1,2,4}.hip

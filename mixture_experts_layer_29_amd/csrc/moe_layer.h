@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void layer_kernel(LayerArgs L) {
 }
 
 // The layer kernel for token bucket TB, selection slots NS (4, 8 or 16 wave
-// slots of 64 experts) and down shape index `shape` (as in pick_down: 0..2 for
+// slots of 64 experts) and down shape index `shape` (0..2 for
 // I = 64, 128, 256, then 2 + I / 512 up to I = 2048); null if none.
 template <int TB>
 const void* layer_fn(int ns, int shape) {

@@ -120,10 +120,13 @@ def test_auto_variant(batch, variant):
     p = moe.Plan(cfg(batch=batch))
     info = p.info()
     assert info.variant == variant
-    # front (router + shared gate/up), [top-k], routed gate/up, down
-    assert info.router_mfma == (1 if batch > 4 else 0)
+    # front (router + shared gate/up), [top-k], routed gate/up, down, [combine]:
+    # above batch 4 the router is an MFMA launch + a top-k launch, and the down
+    # projection is expert-major with a combine launch
+    big = 1 if batch > 4 else 0
+    assert info.router_mfma == big
     assert info.single_launch == 0
-    assert info.n_kernels == 3 + info.router_mfma
+    assert info.n_kernels == 3 + 2 * big
     assert info.layer_grid == 0
     assert info.shared_stream == 0
     assert info.workspace_bytes > 0
@@ -134,11 +137,11 @@ def test_auto_variant(batch, variant):
         assert info.mfma_min_tokens == 0 and info.shared_mfma == 0
     p.destroy()
     p = moe.Plan(cfg(batch=batch, shared_stream=1))
-    assert p.info().n_kernels == 4 + (1 if batch > 4 else 0) and p.info().shared_stream == 1
+    assert p.info().n_kernels == 4 + 2 * big and p.info().shared_stream == 1
     assert p.info().single_launch == 0
     p.destroy()
     p = moe.Plan(cfg(batch=batch, single_launch=moe.SINGLE_OFF))
-    assert p.info().n_kernels == 3 + (1 if batch > 4 else 0) and p.info().single_launch == 0
+    assert p.info().n_kernels == 3 + 2 * big and p.info().single_launch == 0
     p.destroy()
     if batch <= 4:
         p = moe.Plan(cfg(batch=batch, single_launch=moe.SINGLE_REQUIRED))
@@ -190,7 +193,8 @@ def test_profiling_toggle_without_device():
     p = moe.Plan(cfg())
     p.set_profiling(True)
     prof = p.profile_read()
-    assert set(prof) == {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine", "layer"}
+    assert set(prof) == {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine", "layer",
+                         "combine"}
     assert all(v == (0.0, 0) for v in prof.values())
     p.set_profiling(False)
     p.destroy()
