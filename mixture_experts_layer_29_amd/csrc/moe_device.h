@@ -103,6 +103,19 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Wave-wide maximum of unsigned values; masked-off lanes read 0, the identity,
+// so each step is a single DPP-fused v_max_u32.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    int x = (int)v;
+    x = (int)max((uint32_t)x, (uint32_t)dpp_i<0xb1, 0xf>(0, x));   // quad_perm [1,0,3,2]
+    x = (int)max((uint32_t)x, (uint32_t)dpp_i<0x4e, 0xf>(0, x));   // quad_perm [2,3,0,1]
+    x = (int)max((uint32_t)x, (uint32_t)dpp_i<0x141, 0xf>(0, x));  // row_half_mirror
+    x = (int)max((uint32_t)x, (uint32_t)dpp_i<0x140, 0xf>(0, x));  // row_mirror
+    x = (int)max((uint32_t)x, (uint32_t)dpp_i<0x142, 0xa>(0, x));  // row_bcast15
+    x = (int)max((uint32_t)x, (uint32_t)dpp_i<0x143, 0xc>(0, x));  // row_bcast31
+    return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+
 __device__ __forceinline__ int wave_min_int(int v) {
     v = min(v, dpp_i<0xb1, 0xf>(v));
     v = min(v, dpp_i<0x4e, 0xf>(v));
@@ -189,105 +202,90 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // top-k selection, routing weights, bucketing
 // ---------------------------------------------------------------------------
 
-constexpr int kSlots = kMaxExperts / 64;  // logits held per lane
 constexpr int kNone = 0x7fffffff;
 
+// Unsigned key with the order of the float (larger key = larger value; every
+// key of a number, -inf included, is > 0).  -0 and +0 get different keys, so
+// they are compared through the floats where that matters.
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Top-k of one token by one wave.  Slot m of lane l holds the logit of expert
-// (slot0 + m * step) * 64 + l in v[m] (slots past E hold -inf and are never
-// selected).  Each round takes the wave-wide largest remaining logit (DPP
-// max); equal logits go to the lower expert id (ballot, then DPP min when
-// several lanes tie).  Fills sel_e / sel_z in rank order (wave-uniform);
-// rounds that find nothing left give sel_e = -1.
+// m * 64 + l in v[m] (slots at or past E are never selected).  Each round
+// takes the wave-wide largest remaining logit (DPP max over the lanes' current
+// best); equal logits go to the lower expert id (ballot; DPP min when several
+// lanes tie); the winning lane then drops that slot and finds its next best.
+// Lane r < k ends with entry r of the selection (my_e, my_z); the round loop
+// is not unrolled, so its code stays small (the selection runs once per
+// launch, from a cold instruction cache).
 template <int NS>
-__device__ __forceinline__ void topk_wave(const float (&v)[NS], int slot0, int step, int E, int k, int lane,
-                                          int (&sel_e)[kMaxTopK], float (&sel_z)[kMaxTopK]) {
+__device__ __forceinline__ void topk_wave(const float (&v)[NS], int E, int k, int lane, int& my_e, float& my_z) {
     uint32_t avail = 0;
 #pragma unroll
     for (int m = 0; m < NS; ++m)
-        if ((slot0 + m * step) * 64 + lane < E) avail |= 1u << m;
-    float bv = -INFINITY;
-    int be = kNone;
+        if (m * 64 + lane < E) avail |= 1u << m;
+    float bv;      // lane's best remaining logit
+    uint32_t bk;   // its order key, 0 when the lane has nothing left
+    int be;        // its expert id
     auto lane_best = [&]() {
         bv = -INFINITY;
+        bk = 0;
         be = kNone;
 #pragma unroll
-        for (int m = 0; m < NS; ++m)
-            if (((avail >> m) & 1u) && v[m] > bv) { bv = v[m]; be = (slot0 + m * step) * 64 + lane; }
+        for (int m = 0; m < NS; ++m) {
+            const uint32_t km = order_key(v[m]);
+            const bool take = ((avail >> m) & 1u) && km > bk;  // strict: ties keep the lower id
+            bv = take ? v[m] : bv;
+            bk = take ? km : bk;
+            be = take ? m * 64 + lane : be;
+        }
     };
     lane_best();
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-        sel_e[r] = -1;
-        sel_z[r] = -INFINITY;
-        if (r < k) {
-            const float m = wave_max(bv);
-            const unsigned long long bal = __ballot(be != kNone && bv == m);
-            if (bal) {
-                int e;
-                if (__popcll(bal) == 1) e = __builtin_amdgcn_readlane(be, __ffsll(bal) - 1);
-                else e = wave_min_int(((bal >> lane) & 1ull) ? be : kNone);
-                sel_e[r] = e;
-                sel_z[r] = m;
-                if (lane == (e & 63)) {
-#pragma unroll
-                    for (int q = 0; q < NS; ++q)
-                        if ((slot0 + q * step) * 64 + lane == e) avail &= ~(1u << q);
-                    lane_best();
-                }
-            }
+    my_e = -1;
+    my_z = -INFINITY;
+#pragma unroll 1
+    for (int r = 0; r < k; ++r) {
+        const uint32_t mk = wave_max_u32(bk);
+        if (mk == 0) break;
+        // lanes holding the largest logit (the float compare also ties -0 with +0)
+        const float m = __uint_as_float((mk & 0x80000000u) ? (mk & 0x7fffffffu) : ~mk);
+        const unsigned long long bal = __ballot(bk != 0 && bv == m);
+        int e;
+        if (__popcll(bal) == 1) e = __builtin_amdgcn_readlane(be, __ffsll(bal) - 1);
+        else e = (int)~wave_max_u32(((bal >> lane) & 1ull) ? ~(uint32_t)be : 0u);
+        const float ez = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), e & 63));
+        if (lane == r) {
+            my_e = e;
+            my_z = ez;
         }
-    }
-}
-
-// Merges per-wave candidate lists (up to 64 (logit, expert) pairs, one per
-// lane; invalid lanes hold e = kNone) into the top-k, same order and ties.
-__device__ __forceinline__ void topk_merge(float cv, int ce, int k, int lane, int (&sel_e)[kMaxTopK],
-                                           float (&sel_z)[kMaxTopK]) {
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-        sel_e[r] = -1;
-        sel_z[r] = -INFINITY;
-        if (r < k) {
-            const float m = wave_max(cv);
-            const unsigned long long bal = __ballot(ce != kNone && cv == m);
-            if (bal) {
-                int e;
-                if (__popcll(bal) == 1) e = __builtin_amdgcn_readlane(ce, __ffsll(bal) - 1);
-                else e = wave_min_int(((bal >> lane) & 1ull) ? ce : kNone);
-                sel_e[r] = e;
-                sel_z[r] = m;
-                if (ce == e) { cv = -INFINITY; ce = kNone; }
-            }
+        if (be == e) {  // the winner drops the slot and takes its next best
+            avail &= ~(1u << (e >> 6));
+            lane_best();
         }
     }
 }
 
 // Routing weights of the selected logits (softmax or sigmoid, optional
-// renormalisation over the selection, times routed_scale); lane r < k
-// computes and writes entry r of the token's topk_idx / topk_w row (and of
-// s_pair_e when given).  zrow (the token's logits, readable by this wave) is
-// read only for a softmax without renormalisation, whose denominator runs
-// over all E experts.
-__device__ __forceinline__ void route_token(const RouterArgs& a, int t, int lane, const float* zrow,
-                                            const int (&sel_e)[kMaxTopK], const float (&sel_z)[kMaxTopK],
-                                            int32_t* s_pair_e) {
+// renormalisation over the selection, times routed_scale).  Lane r < k holds
+// entry r of the selection (expert er, logit zr); zmax is the largest
+// selected logit.  Writes the token's topk_idx / topk_w row (and s_pair_e
+// when given).  zrow (the token's logits, readable by this wave) is read only
+// for a softmax without renormalisation, whose denominator runs over all E.
+__device__ __forceinline__ void route_one(const RouterArgs& a, int t, int lane, const float* zrow, int er, float zr,
+                                          float zmax, int32_t* s_pair_e) {
     const int k = a.k, E = a.E;
-    float zr = -INFINITY;
-    int er = -1;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r)
-        if (lane == r) { zr = sel_z[r]; er = sel_e[r]; }
     const bool mine = lane < k;
-    const float m = sel_z[0];
     float w;
     if (a.score_fn == 0) {
-        const float ex = mine ? expf(zr - m) : 0.0f;
+        const float ex = mine ? expf(zr - zmax) : 0.0f;
         float den;
         if (a.renormalize) {
             den = wave_sum(ex);
         } else {
             float part = 0.0f;
-            for (int e = lane; e < E; e += 64) part += expf(ld_dev(zrow + e) - m);
+            for (int e = lane; e < E; e += 64) part += expf(ld_dev(zrow + e) - zmax);
             den = wave_sum(part);
         }
         w = ex / den;
@@ -419,72 +417,42 @@ __device__ __forceinline__ void bucket_block(const RouterArgs& a, const int32_t*
     if (tid == 0) bucket_meta(a, ftot, *s_nmfma, npairs, ctot);
 }
 
-// Selection for tokens t0 + wave of this workgroup.
+// Selection for tokens t0 + wave of this workgroup, one wave per token.
 // src: per-token logit rows (E floats); with `from_acc` they are split-K
 // accumulators: the bias is added, the sum stored to a.z and the accumulator
-// cleared.  A single token is ranked by all four waves (each over every
-// fourth slot) and merged by wave 0.  Ends with a workgroup barrier, after
-// which s_pair_e (if given) holds the selected ids of the workgroup's tokens.
+// cleared.  Ends with a workgroup barrier, after which s_pair_e (if given)
+// holds the selected ids of the workgroup's tokens.
 template <int NS>
 __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float* src, const float* bias,
-                                              bool from_acc, int32_t* s_pair_e, int32_t* s_cand_e,
-                                              float* s_cand_z, float* s_z) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                              bool from_acc, int32_t* s_pair_e) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = a.E, B = a.B, k = a.k;
-    int sel_e[kMaxTopK];
-    float sel_z[kMaxTopK];
-    auto fetch = [&](float* row, float* zout, int e) {
-        float v = ld_dev(row + e);
-        if (from_acc) {
-            v += bias ? bias[e] : 0.0f;
-            st_dev(zout + e, v);
-            st_dev(row + e, 0.0f);
-        }
-        return v;
-    };
-    if (B == 1) {
-        constexpr int NQ = (NS + 3) / 4;
-        float v[NQ];
+    const int t = t0 + wave;
+    if (t < B) {
+        float* row = src + (size_t)t * E;
+        float* zo = a.z + (size_t)t * E;
+        float v[NS];
 #pragma unroll
-        for (int m = 0; m < NQ; ++m) {
-            const int e = (wave + 4 * m) * 64 + lane;
-            v[m] = (e < E) ? fetch(src, a.z, e) : -INFINITY;
-            if (e < E) s_z[e] = v[m];
-        }
-        topk_wave<NQ>(v, wave, 4, E, k, lane, sel_e, sel_z);
-        if (lane < k) {
-            int ce = kNone;
-            float cz = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < kMaxTopK; ++r)
-                if (lane == r) { ce = sel_e[r] >= 0 ? sel_e[r] : kNone; cz = sel_z[r]; }
-            s_cand_e[wave * kMaxTopK + lane] = ce;
-            s_cand_z[wave * kMaxTopK + lane] = cz;
-        }
-        __syncthreads();
-        if (wave == 0) {
-            const int r = lane % kMaxTopK;
-            const bool ok = r < k;
-            topk_merge(ok ? s_cand_z[lane] : -INFINITY, ok ? s_cand_e[lane] : kNone, k, lane, sel_e, sel_z);
-            route_token(a, 0, lane, s_z, sel_e, sel_z, s_pair_e);
-        }
-    } else {
-        const int t = t0 + wave;
-        if (t < B) {
-            float* row = src + (size_t)t * E;
-            float* zo = a.z + (size_t)t * E;
-            float v[NS];
-#pragma unroll
-            for (int m = 0; m < NS; ++m) {
-                const int e = m * 64 + lane;
-                v[m] = (e < E) ? fetch(row, zo, e) : -INFINITY;
+        for (int m = 0; m < NS; ++m) {
+            const int e = m * 64 + lane;
+            float x = -INFINITY;
+            if (e < E) {
+                x = ld_dev(row + e);
+                if (from_acc) {
+                    x += bias ? bias[e] : 0.0f;
+                    st_dev(zo + e, x);
+                    st_dev(row + e, 0.0f);
+                }
             }
-            topk_wave<NS>(v, 0, 1, E, k, lane, sel_e, sel_z);
-            // a full softmax reads the token's logits back: from_acc rows are in a.z (this
-            // wave's stores, complete after the wait)
-            __builtin_amdgcn_s_waitcnt(0);
-            route_token(a, t, lane, from_acc ? zo : row, sel_e, sel_z, s_pair_e);
+            v[m] = x;
         }
+        int my_e;
+        float my_z;
+        topk_wave<NS>(v, E, k, lane, my_e, my_z);
+        // a full softmax reads the token's logits back: from_acc rows are in a.z (this
+        // wave's stores, complete after the wait)
+        __builtin_amdgcn_s_waitcnt(0);
+        route_one(a, t, lane, from_acc ? zo : row, my_e, my_z, __shfl(my_z, 0, 64), s_pair_e);
     }
     __syncthreads();
 }

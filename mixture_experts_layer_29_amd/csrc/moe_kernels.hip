@@ -50,9 +50,6 @@ __global__ __launch_bounds__(256) void front_small_kernel(FrontArgs f) {
         return;
     }
     __shared__ int32_t s_pair_e[4 * kMaxTopK];
-    __shared__ int32_t s_cand_e[4 * kMaxTopK];
-    __shared__ float s_cand_z[4 * kMaxTopK];
-    __shared__ float s_z[kMaxExperts];
     __shared__ int s_flag;
 
     router_rows<TB, SELECT>(a, blockIdx.x, s_x);
@@ -61,8 +58,7 @@ __global__ __launch_bounds__(256) void front_small_kernel(FrontArgs f) {
     // the last router workgroup to arrive selects and buckets
     if (!arrive_last(reinterpret_cast<unsigned*>(&a.meta[M_ROUTER_CNT]), f.router_blocks, &s_flag)) return;
 
-    select_tokens<NS>(a, 0, a.z, nullptr, false, s_pair_e, s_cand_e, s_cand_z, s_z);
-    __syncthreads();
+    select_tokens<NS>(a, 0, a.z, nullptr, false, s_pair_e);
     if ((threadIdx.x >> 6) == 0) bucket_wave(a, s_pair_e, threadIdx.x & 63);
 }
 
@@ -87,17 +83,13 @@ __global__ __launch_bounds__(256) void topk_bucket_kernel(RouterArgs a) {
     __shared__ int32_t s_pair_e[kMaxBatch * kMaxTopK];
     __shared__ int32_t s_rank[kMaxBatch * kMaxTopK];
     __shared__ int32_t s_cnt[kMaxExperts];
-    __shared__ int32_t s_cand_e[4 * kMaxTopK];
-    __shared__ float s_cand_z[4 * kMaxTopK];
-    __shared__ float s_z[kMaxExperts];
     __shared__ int32_t s_tmp[8];
     __shared__ int32_t s_nmfma;
     __shared__ int s_flag;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int B = a.B, np = B * a.k;
     const bool single = gridDim.x == 1;
-    select_tokens<NS>(a, blockIdx.x * 4, a.zacc, a.bias, true, single ? s_pair_e : nullptr, s_cand_e, s_cand_z,
-                      s_z);
+    select_tokens<NS>(a, blockIdx.x * 4, a.zacc, a.bias, true, single ? s_pair_e : nullptr);
     if (!single) {
         if (!arrive_last(reinterpret_cast<unsigned*>(&a.meta[M_ROUTER_CNT]), gridDim.x, &s_flag)) return;
         for (int p = tid; p < np; p += 256) s_pair_e[p] = ld_dev(a.topk_idx + p);

@@ -53,9 +53,7 @@ template <int TB, int NS, int LPR, int NQ, int RP>
 __global__ __launch_bounds__(256) void layer_kernel(LayerArgs L) {
     extern __shared__ __align__(16) unsigned char s_dyn[];  // x staging, then h rows of down tasks
     __shared__ int32_t s_pair_e[4 * kMaxTopK];
-    __shared__ int32_t s_cand_e[4 * kMaxTopK];
-    __shared__ float s_cand_z[4 * kMaxTopK];
-    __shared__ float s_z[kMaxExperts];
+
     __shared__ float s_acc[4 * DownShape<LPR, NQ, RP>::R];  // batch <= 4
     __shared__ int s_task, s_flag;
     uint16_t* s_x = reinterpret_cast<uint16_t*>(s_dyn);
@@ -75,7 +73,7 @@ __global__ __launch_bounds__(256) void layer_kernel(LayerArgs L) {
         if (t < t_sgu) {
             router_rows<TB, true>(a, t, s_x);
             if (arrive_last(reinterpret_cast<unsigned*>(&meta[M_ROUTER_CNT]), L.n_router, &s_flag)) {
-                select_tokens<NS>(a, 0, a.z, nullptr, false, s_pair_e, s_cand_e, s_cand_z, s_z);
+                select_tokens<NS>(a, 0, a.z, nullptr, false, s_pair_e);
                 if ((tid >> 6) == 0) bucket_wave(a, s_pair_e, tid & 63);
                 publish(&meta[M_SEL]);
             }
