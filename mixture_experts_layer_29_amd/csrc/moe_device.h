@@ -188,6 +188,36 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total, i
 }
 
 
+constexpr int kSpinLimit = 1 << 20;  // bounded waits: a lost hand-off ends in ERR_TIMEOUT, not a hang
+
+// Adds one to *counter once every wave's coherent stores (st_dev) have
+// completed, so a workgroup that sees the count can read them with ld_dev.
+__device__ __forceinline__ void publish(int32_t* counter) {
+    stores_done_barrier();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Blocks the workgroup until *counter >= target (bounded wait).  Loads after
+// it are issued after the counter was seen (barrier), and hand-off data is
+// read with coherent loads, so no cache invalidation is needed.
+__device__ __forceinline__ void wait_count(const int32_t* counter, int target, int32_t* meta) {
+    if (threadIdx.x == 0) {
+        int it = 0;
+        while (ld_dev(counter) < target) {
+            if (++it > kSpinLimit) {
+                atomicOr(&meta[M_ERR], ERR_TIMEOUT);
+                break;
+            }
+            // back off: many waiting workgroups polling one address slow the
+            // memory channel it lives on
+            if (it < 4) __builtin_amdgcn_s_sleep(2);
+            else if (it < 16) __builtin_amdgcn_s_sleep(8);
+            else __builtin_amdgcn_s_sleep(32);
+        }
+    }
+    __syncthreads();
+}
+
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
 // fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
@@ -789,12 +819,11 @@ enum DownMode : int {
 // wait() runs after the first chunk of (static) weights is requested and
 // before any h is read: the single-launch layer blocks there until the gate/up
 // tasks are done.  s_h: dynamic LDS; s_acc: kMaxBatch * R floats of LDS.
-template <int LPR, int NQ, int RP, bool HLDS, int MODE, class Wait>
+// COH: routing, work lists and h may come from other workgroups of this
+// launch (coherent loads); otherwise from an earlier launch (cached loads).
+template <int LPR, int NQ, int RP, bool HLDS, int MODE, bool COH, class Wait>
 __device__ __forceinline__ void down_rows(const DownArgs& a, int row_block, float* s_h, float* s_acc, Wait&& wait) {
     constexpr int mode = MODE;
-    // routing, work lists and h come from an earlier launch (DOWN_ALL: plain
-    // cached loads) or from other workgroups of this launch (coherent loads)
-    constexpr bool COH = MODE != DOWN_ALL;
     auto ldi = [](const int* p) { if constexpr (COH) return ld_dev(p); else return *p; };
     auto ldf = [](const float* p) { if constexpr (COH) return ld_dev(p); else return *p; };
     auto ld4 = [](const float* p) {

@@ -142,7 +142,7 @@ template <int LPR, int NQ, int RP, bool HLDS>
 __global__ __launch_bounds__(256) void down_combine_kernel(DownArgs a) {
     extern __shared__ __align__(16) float s_h[];
     __shared__ float s_acc[kMaxBatch * DownShape<LPR, NQ, RP>::R];
-    down_rows<LPR, NQ, RP, HLDS, DOWN_ALL>(a, blockIdx.x, s_h, s_acc, [] {});
+    down_rows<LPR, NQ, RP, HLDS, DOWN_ALL, false>(a, blockIdx.x, s_h, s_acc, [] {});
 }
 
 // ---------------------------------------------------------------------------

@@ -11,32 +11,6 @@ namespace moe {
 // single-launch layer (batch <= 4)
 // ---------------------------------------------------------------------------
 
-constexpr int kSpinLimit = 1 << 20;  // bounded waits: a lost hand-off ends in ERR_TIMEOUT, not a hang
-
-// Adds one to *counter once every wave's coherent stores (st_dev) have
-// completed, so a workgroup that sees the count can read them with ld_dev.
-__device__ __forceinline__ void publish(int32_t* counter) {
-    stores_done_barrier();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Blocks the workgroup until *counter >= target (bounded wait).  Loads after
-// it are issued after the counter was seen (barrier), and hand-off data is
-// read with coherent loads, so no cache invalidation is needed.
-__device__ __forceinline__ void wait_count(const int32_t* counter, int target, int32_t* meta) {
-    if (threadIdx.x == 0) {
-        int it = 0;
-        while (ld_dev(counter) < target) {
-            if (++it > kSpinLimit) {
-                atomicOr(&meta[M_ERR], ERR_TIMEOUT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-    }
-    __syncthreads();
-}
-
 // Tasks, in an order where every dependency points to a lower index:
 //   router rows (the last to finish selects, buckets and publishes M_SEL),
 //   shared gate/up tiles, shared down row blocks (fp32 into s_out),
@@ -84,7 +58,7 @@ __global__ __launch_bounds__(256) void layer_kernel(LayerArgs L) {
             else gemv_gateup_tile<TB>(L.f.s, L.f.s.w, 0, a.B, local, s_x);
             if (did) publish(&meta[M_SGU_DONE]);
         } else if (t < t_gu) {
-            down_rows<LPR, NQ, RP, true, DOWN_SHARED>(L.d, t - t_sdown, s_h, s_acc,
+            down_rows<LPR, NQ, RP, true, DOWN_SHARED, true>(L.d, t - t_sdown, s_h, s_acc,
                                          [&] { wait_count(&meta[M_SGU_DONE], L.sgu_expect, meta); });
             publish(&meta[M_SDOWN_DONE]);
         } else if (t < t_down) {
@@ -110,7 +84,7 @@ __global__ __launch_bounds__(256) void layer_kernel(LayerArgs L) {
             }
         } else {
             wait_count(&meta[M_SEL], 1, meta);
-            down_rows<LPR, NQ, RP, true, DOWN_ROUTED>(L.d, t - t_down, s_h, s_acc, [&] {
+            down_rows<LPR, NQ, RP, true, DOWN_ROUTED, true>(L.d, t - t_down, s_h, s_acc, [&] {
                 wait_count(&meta[M_GU_DONE], ld_dev(meta + M_GEMV_TILES) + ld_dev(meta + M_MFMA_TILES), meta);
                 wait_count(&meta[M_SDOWN_DONE], L.n_sdown, meta);
             });
