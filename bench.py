@@ -32,6 +32,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+
+# HBM traffic of the routed gate/up kernel at batch 1 from rocprofv3 counters
+# (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the scales a 2 GiB device copy gives
+# those counters); taken on the kernel sources with these SHA-1s and reported
+# only while the sources are unchanged (profiles/*hbm_traffic.md).
+GATEUP_TRAFFIC = {"fetch_kib": 28777.6, "write_kib": 64.0, "fetch_scale": 2.0, "write_scale": 1.0,
+                  "sources": {"moe_device.h": "890e32cc8e28f6e4e6fd990f8b831643ff96583f",
+                              "moe_kernels.hip": "294b925ee863e296884ba17f5f0e7751692fa7a1"}}
+
+
+def gateup_traffic_bytes():
+    """Counter-measured HBM bytes per launch of the routed gate/up kernel, or
+    None when its sources changed since the counters were taken."""
+    import hashlib
+    csrc = os.path.join(ROOT, "mixture_experts_layer_29_amd", "csrc")
+    for name, digest in GATEUP_TRAFFIC["sources"].items():
+        with open(os.path.join(csrc, name), "rb") as fh:
+            if hashlib.sha1(fh.read()).hexdigest() != digest:
+                return None
+    t = GATEUP_TRAFFIC
+    return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
 METRIC = "MoE decode layer µs & tokens/s at batch 1/16/64; achieved HBM GB/s vs peak"
 
 
@@ -46,6 +67,8 @@ def parse():
     ap.add_argument("--sweep", type=str, default="16,64", help="extra batch sizes ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only the device copy of a 2 GiB buffer (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -220,6 +243,10 @@ def main():
     import synthetic
 
     torch.cuda.set_device(0)
+    if args.copy_only:
+        print(json.dumps({"copy_GBps": copy_gbps(torch), "bytes_read_per_copy": 2 << 30,
+                          "bytes_written_per_copy": 2 << 30}))
+        return
     wl = synthetic.TP8
     log("drawing %d TP8-shard layers on the device" % args.layers)
     layers = [synthetic.device_layer(wl, "cuda", layer=i) for i in range(args.layers)]
@@ -273,7 +300,7 @@ def main():
         "copy_GBps": cg,
         "roofline": {"kernel": "gateup_routed", "bound": "hbm", "achieved": gu["GBps"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gu["GBps"] / HBM_PEAK_GBPS,
-                     "traffic": None, "avg_us": gu["avg_us"], "bytes_per_launch": gu["bytes_per_launch"]},
+                     "traffic": gateup_traffic_bytes(), "avg_us": gu["avg_us"], "bytes_per_launch": gu["bytes_per_launch"]},
         "cpu_baseline": cpu,
         "sweep": sweep,
     }
