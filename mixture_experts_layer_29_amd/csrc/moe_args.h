@@ -35,6 +35,7 @@ constexpr int kPairsPerGemvTile = 4;
 constexpr int kPairsPerMfmaTile = 64;
 constexpr int kMaxGemvUnits = 16;  // 16-byte units per lane held in registers by a GEMV wave
 constexpr int kGemvLdsBytes = 60 * 1024;  // x staging budget of a GEMV workgroup
+constexpr int kXStage = 4;                 // x units per thread requested ahead of a GEMV's weights
 constexpr int kRouterRowsPerMfmaTile = 64;
 constexpr int kDownHStage = 32 * 1024;  // LDS bytes for a staged batch of h rows in down
 

@@ -492,7 +492,7 @@ __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float
 // plus the shared expert's gate/up in trailing workgroups
 // ---------------------------------------------------------------------------
 
-template <int TB>
+template <int TB, bool COH = false>
 __device__ __forceinline__ void gemv_gateup_tile(const GateUpArgs& a, const uint16_t* W, int off, int T, int local,
                                  uint16_t* s_x);
 template <int NTM>
@@ -514,6 +514,17 @@ __device__ __forceinline__ void router_rows(const RouterArgs& a, int blk, uint16
     float acc[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
+    // x ([B][H], contiguous) is staged in LDS: the first kXStage units per
+    // thread are requested before the weights, since vector memory loads
+    // complete in issue order and a store of x issued after the weights would
+    // wait for them; any rest follows them.
+    const int nx = B * units;
+    u32x4 xr[kXStage];
+#pragma unroll
+    for (int q = 0; q < kXStage; ++q) {
+        const int i = tid + 256 * q;
+        xr[q] = ld16(a.x + (size_t)(i < nx ? i : 0) * 8);
+    }
     for (int base = 0; base < nu; base += kMaxGemvUnits) {
         u32x4 w[kMaxGemvUnits];
 #pragma unroll
@@ -521,11 +532,11 @@ __device__ __forceinline__ void router_rows(const RouterArgs& a, int blk, uint16
             const int u = (base + q) * 64 + lane;
             w[q] = (row_ok && u < units) ? ld16(wrow + u * 8) : zero;
         }
-        if (base == 0) {  // stage x while the weight loads are in flight
-            for (int i = tid; i < B * units; i += 256) {
-                const int t = i / units, u = i - t * units;
-                st16(s_x + t * H + u * 8, ld16(a.x + (size_t)t * H + u * 8));
-            }
+        if (base == 0) {
+#pragma unroll
+            for (int q = 0; q < kXStage; ++q)
+                if (tid + 256 * q < nx) st16(s_x + (tid + 256 * q) * 8, xr[q]);
+            for (int i = tid + 256 * kXStage; i < nx; i += 256) st16(s_x + i * 8, ld16(a.x + (size_t)i * 8));
             __syncthreads();
         }
 #pragma unroll
@@ -624,7 +635,7 @@ __device__ __forceinline__ void router_mfma_tile(const RouterArgs& a, int tile) 
 // Full-K GEMV tile: wave w computes row pair i = 4*local + w (gate row i and
 // up row n+i) for the entry's T <= TB tokens, whose activations the workgroup
 // stages in LDS after issuing its weight loads.
-template <int TB>
+template <int TB, bool COH>
 __device__ __forceinline__ void gemv_gateup_tile(const GateUpArgs& a, const uint16_t* W, int off, int T, int local,
                                  uint16_t* s_x) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -636,6 +647,22 @@ __device__ __forceinline__ void gemv_gateup_tile(const GateUpArgs& a, const uint
     float ag[TB], au[TB];
 #pragma unroll
     for (int j = 0; j < TB; ++j) { ag[j] = 0.0f; au[j] = 0.0f; }
+    // The entry's token rows.  Staged launches read the work list of an
+    // earlier launch with scalar loads (their counter is separate from the
+    // weights'); the single launch reads it coherently, per unit.
+    const int nx = T * units;
+    int tk[4] = {0, 0, 0, 0};
+    if constexpr (!COH && TB <= 4) {
+#pragma unroll
+        for (int j = 0; j < TB; ++j) tk[j] = j < T ? uni(a.perm[off + j]) / a.pair_div : 0;
+    }
+    auto xsrc = [&](int idx) {  // unit idx of the staged [T][H] activations
+        const int j = idx / units, uu = idx - j * units;
+        int t;
+        if constexpr (!COH && TB <= 4) t = j == 0 ? tk[0] : j == 1 ? tk[1] : j == 2 ? tk[2] : tk[3];
+        else t = (COH ? ld_dev(a.perm + off + j) : a.perm[off + j]) / a.pair_div;
+        return a.x + (size_t)t * H + uu * 8;
+    };
     for (int base = 0; base < nu; base += kMaxGemvUnits) {
         u32x4 wg[kMaxGemvUnits], wu[kMaxGemvUnits];
 #pragma unroll
@@ -645,12 +672,20 @@ __device__ __forceinline__ void gemv_gateup_tile(const GateUpArgs& a, const uint
             wg[q] = ok ? ld16(g + uu * 8) : zero;
             wu[q] = ok ? ld16(u + uu * 8) : zero;
         }
-        if (base == 0) {  // stage the tokens' activations while the weights stream in
-            for (int idx = tid; idx < T * units; idx += 256) {
-                const int j = idx / units, uu = idx - j * units;
-                const int tok = ld_dev(a.perm + off + j) / a.pair_div;
-                st16(s_x + j * H + uu * 8, ld16(a.x + (size_t)tok * H + uu * 8));
+        if (base == 0) {
+            // activations to LDS: all of this thread's first kXStage units are
+            // requested right behind the weights and stored once they are in
+            // (loads complete in issue order), so x costs no extra round trip
+            u32x4 xr[kXStage];
+#pragma unroll
+            for (int q = 0; q < kXStage; ++q) {
+                const int idx = tid + 256 * q;
+                xr[q] = ld16(xsrc(idx < nx ? idx : 0));
             }
+#pragma unroll
+            for (int q = 0; q < kXStage; ++q)
+                if (tid + 256 * q < nx) st16(s_x + (tid + 256 * q) * 8, xr[q]);
+            for (int idx = tid + 256 * kXStage; idx < nx; idx += 256) st16(s_x + idx * 8, ld16(xsrc(idx)));
             __syncthreads();
         }
 #pragma unroll

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void layer_kernel(LayerArgs L) {
                 } else {
                     const uint16_t* W = g.w + (size_t)e * (size_t)g.expert_stride;
                     if (mfma) counted = mfma_gateup_tile<1>(g, W, entry, off, T, local);
-                    else gemv_gateup_tile<TB>(g, W, off, T, local, s_x);
+                    else gemv_gateup_tile<TB, true>(g, W, off, T, local, s_x);
                 }
                 if (counted) publish(&meta[M_GU_DONE]);
             }
