@@ -135,7 +135,6 @@ struct DownXArgs {
     int32_t max_act;         // routed entries of the grid
     int32_t nsh;             // shared column blocks (Is / I, 0 without a shared expert)
     int32_t mfma_min_tokens; // entries with at least this many tokens use MFMA (0: never)
-    int32_t gemv_max_tokens; // GEMV tiles stage at most this many tokens' h in LDS
 };
 
 // First launch of a layer: the router (GEMV for batch <= 4, split-K MFMA
@@ -191,7 +190,7 @@ int front_router_blocks(const RouterArgs& a, bool small_router);
 KernelPick pick_topk(const RouterArgs& a);
 KernelPick pick_gateup(const GateUpArgs& a, int max_entries, int gemv_tokens);
 constexpr int kDownXRows = 256;           // output rows per expert-major down tile
-constexpr int kDownXLds = 32 * 1024;      // LDS for a GEMV tile's staged h rows
+constexpr int kDownXLds = 64 * 1024;      // LDS for a down tile's staged h rows
 KernelPick pick_down_x(const DownXArgs& a);
 KernelPick pick_combine(const DownXArgs& a);
 // Output-stationary down (down_rows over all entries) for small batches.

@@ -326,7 +326,6 @@ void fill_static_args(moe_decode_plan_s* p) {
     x.max_act = p->max_act;
     x.nsh = c.shared_inter / c.inter;
     x.mfma_min_tokens = p->mfma_min;
-    x.gemv_max_tokens = std::min(32, kDownXLds / (4 * c.inter));
 
     if (p->fused) {
         LayerArgs& l = p->la;

@@ -54,6 +54,23 @@ __device__ __forceinline__ float dot8_f32(u32x4 w, const float4 h0, const float4
     return acc;
 }
 
+// acc + sum_{i<8} w_i * h_i, w bf16, h given as bf16 hi + lo parts (h ~= hi +
+// lo to ~2^-16 relative): two v_dot2_f32_bf16 per weight pair, no unpacking.
+__device__ __forceinline__ float dot8_hilo(u32x4 w, u32x4 hi, u32x4 lo, float acc) {
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+    const uint32_t h0 = hi[0], h1 = hi[1], h2 = hi[2], h3 = hi[3];
+    const uint32_t l0 = lo[0], l1 = lo[1], l2 = lo[2], l3 = lo[3];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(h0), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(l0), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(h1), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(l1), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(h2), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(l2), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(h3), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(l3), acc, false);
+    return acc;
+}
+
 // Wave-wide reductions through DPP (quad permutes, row mirrors, row
 // broadcasts 15/31); the result is read from lane 63 and is wave-uniform.
 // Lanes outside a step's row mask receive `old`: 0 for sums, v for max/min.

@@ -168,17 +168,23 @@ __device__ __forceinline__ void split_bf16x8(const float4 f0, const float4 f1, u
 // expert with T tokens, or a shared column block with all B tokens); wave w
 // owns the 64-row band r0 + 64w.  Token j's h row is hsrc + j * hstride (I
 // floats); its partial output row is dst + s_dsto[j] (H floats).
-//  GEMV (T <= gemv_max_tokens, no MFMA): h staged in LDS; LPR lanes per row,
-//    NQ 16-byte units per lane per row; the band's rows are loaded in batches
-//    of 16 units per lane, the next batch requested before the current one is
-//    used.
-//  MFMA (else): per 32-column step, each wave multiplies its four 16-row
-//    groups (A = W2 rows) by h^T (B, split into bf16 hi + lo, loaded once per
-//    step for all four groups) with mfma_f32_16x16x32_bf16.
+// Order of work, so that the weights are requested after one scalar round
+// trip and everything else rides behind them (vector memory loads complete in
+// issue order): work-list fields (read together with the entry count), then
+// the band's weights, then h (to LDS) and the rows' output offsets, barrier,
+// compute.
+//  GEMV (few tokens, h in LDS): LPR lanes per row, NQ 16-byte units per lane
+//    per row; the band's rows in batches of 16 units per lane, two batches in
+//    flight, a batch re-requested as soon as the one before it is used.
+//  MFMA (else, or when h does not fit LDS): per 32-column step, each wave
+//    multiplies its four 16-row groups (A = W2 rows, all steps of a 256-column
+//    chunk requested at once) by h^T (B, split into bf16 hi + lo) with
+//    mfma_f32_16x16x32_bf16.
 // The partials are combined by combine_kernel, the next launch.
 template <int LPR, int NQ>
 __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
-    extern __shared__ __align__(16) float s_h[];  // [T][I] (GEMV tiles)
+    // h split into bf16 hi and lo parts when it fits: pairs [T][I/2] each
+    extern __shared__ __align__(16) uint32_t s_hh[];
     __shared__ int s_dsto[kMaxBatch];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = a.H, I = a.I, B = a.B, k = a.k;
@@ -187,29 +193,27 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
     const int r0 = rb * kDownXRows;
     const int band = r0 + 64 * wave;
     const bool band_ok = band < H;  // H is a multiple of 64
+    const bool routed = ent < a.max_act;
+    const int ent_c = routed ? ent : 0;  // the lists are valid memory for every grid entry
     const int nact = uni(*a.n_act);
+    const int e_r = uni(a.act_e[ent_c]), off_r = uni(a.act_off[ent_c]), end_r = uni(a.act_off[ent_c + 1]);
 
     const uint16_t* W;
     const float* hsrc;
     float* dst;
     int ld, hstride, T;
-    if (ent < a.max_act) {
-        if (ent >= nact) {
-            return;
-        }
-        int e = uni(a.act_e[ent]);
-        const int off = uni(a.act_off[ent]);
-        T = uni(a.act_off[ent + 1]) - off;
-        if ((unsigned)e >= (unsigned)a.n_experts || off < 0 || T < 1 || off + T > B * k || T > kMaxBatch) {
+    if (routed) {
+        if (ent >= nact) return;
+        T = end_r - off_r;
+        if ((unsigned)e_r >= (unsigned)a.n_experts || off_r < 0 || T < 1 || off_r + T > B * k || T > kMaxBatch) {
             if (tid == 0 && rb == 0) atomicOr(&a.meta[M_ERR], ERR_TILE);
             return;
         }
-        W = a.w2 + (size_t)e * H * I;
+        W = a.w2 + (size_t)e_r * H * I;
         ld = I;
-        hsrc = a.h + (size_t)(T ? off : 0) * I;
+        hsrc = a.h + (size_t)off_r * I;
         hstride = I;
         dst = a.part;
-        if (tid < T) s_dsto[tid] = a.perm[off + tid] * H;
     } else {
         const int v = ent - a.max_act;
         W = a.s2 + (size_t)v * I;
@@ -218,12 +222,35 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
         hstride = a.Is;
         T = B;
         dst = a.part_s;
-        if (tid < B) s_dsto[tid] = (v * B + tid) * H;
     }
-    const bool mfma = (a.mfma_min_tokens > 0 && T >= a.mfma_min_tokens) || T > a.gemv_max_tokens;
+    const bool h_lds = (size_t)T * I * 4 <= (size_t)kDownXLds;
+    const bool mfma = (a.mfma_min_tokens > 0 && T >= a.mfma_min_tokens) || !h_lds;
     const u32x4 zero = u32x4{0, 0, 0, 0};
 
-    if (T > 0 && !mfma) {
+    uint32_t* s_hl = s_hh + (size_t)T * I / 2;
+    // h rows to LDS as bf16 hi + lo pairs (when they fit) and the tokens'
+    // output row offsets; called once the band's first weights are requested
+    auto stage = [&]() {
+        if (tid < T) s_dsto[tid] = (routed ? a.perm[off_r + tid] : (ent - a.max_act) * B + tid) * H;
+        if (h_lds) {
+            const int I4 = I / 4;
+            for (int i = tid; i < T * I4; i += 256) {
+                const int j = i / I4, c4 = i - j * I4;
+                const float4 v = *reinterpret_cast<const float4*>(hsrc + (size_t)j * hstride + 4 * c4);
+                const uint32_t h0 = f32_to_bf16_rne(v.x), h1 = f32_to_bf16_rne(v.y);
+                const uint32_t h2 = f32_to_bf16_rne(v.z), h3 = f32_to_bf16_rne(v.w);
+                const uint32_t l0 = f32_to_bf16_rne(v.x - __uint_as_float(h0 << 16));
+                const uint32_t l1 = f32_to_bf16_rne(v.y - __uint_as_float(h1 << 16));
+                const uint32_t l2 = f32_to_bf16_rne(v.z - __uint_as_float(h2 << 16));
+                const uint32_t l3 = f32_to_bf16_rne(v.w - __uint_as_float(h3 << 16));
+                reinterpret_cast<uint2*>(s_hh)[i] = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
+                reinterpret_cast<uint2*>(s_hl)[i] = uint2{l0 | (l1 << 16), l2 | (l3 << 16)};
+            }
+        }
+        __syncthreads();
+    };
+
+    if (!mfma) {
         constexpr int RW = 64 / LPR, P = 64 / RW;            // rows per pass, passes per band
         constexpr int QB = (16 / NQ) < P ? 16 / NQ : P;      // passes per batch of loads
         const int rw = lane / LPR, c = lane % LPR;
@@ -241,19 +268,11 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
         // without copies and each batch's loads are waited for only when used
         u32x4 wbuf[2][QB][NQ];
         load(0, wbuf[0]);
-        {   // stage h while the first batch of weights is in flight
-            const int I4 = I / 4;
-            float4* d = reinterpret_cast<float4*>(s_h);
-            for (int i = tid; i < T * I4; i += 256) {
-                const int j = i / I4, c4 = i - j * I4;
-                d[i] = *reinterpret_cast<const float4*>(hsrc + (size_t)j * hstride + 4 * c4);
-            }
-            __syncthreads();
-        }
+        if (QB < P) load(QB, wbuf[1]);
+        stage();
 #pragma unroll
         for (int q0 = 0; q0 < P; q0 += QB) {
             u32x4 (&wa)[QB][NQ] = wbuf[(q0 / QB) & 1];
-            if (q0 + QB < P) load(q0 + QB, wbuf[((q0 / QB) + 1) & 1]);
             if (band_ok) {
 #pragma unroll
                 for (int q = 0; q < QB; ++q) {
@@ -263,9 +282,9 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
                             float acc = 0.0f;
 #pragma unroll
                             for (int u = 0; u < NQ; ++u) {
-                                const float4* hp =
-                                    reinterpret_cast<const float4*>(s_h + (size_t)j * I + 8 * (c + LPR * u));
-                                acc = dot8_f32(wa[q][u], hp[0], hp[1], acc);
+                                const size_t pe = ((size_t)j * I + 8 * (c + LPR * u)) / 2;  // pair index
+                                acc = dot8_hilo(wa[q][u], *reinterpret_cast<const u32x4*>(s_hh + pe),
+                                                *reinterpret_cast<const u32x4*>(s_hl + pe), acc);
                             }
                             acc = group_sum<LPR>(acc);
                             if (c == LPR - 1) dst[s_dsto[j] + row] = acc;
@@ -273,9 +292,9 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
                     }
                 }
             }
+            if (q0 + 2 * QB < P) load(q0 + 2 * QB, wa);
         }
-    } else if (T > 0) {
-        __syncthreads();  // s_dsto
+    } else {
         const int tl = lane & 15, kq = lane >> 4;
         const int NT = (T + 15) >> 4;
         const uint16_t* arow = W + (size_t)(band + tl) * ld + 8 * kq;  // group g: + 16 g rows
@@ -292,40 +311,40 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
         for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) acc[g][tt] = f32x4{0, 0, 0, 0};
-        constexpr int nsteps = LPR * NQ / 4;  // I / 32
+        constexpr int NSC = (LPR * NQ / 4) < 8 ? LPR * NQ / 4 : 8;  // 32-column steps per chunk (I / 32, at most 8)
+        for (int c0 = 0; c0 < I; c0 += 32 * NSC) {
+            u32x4 A[NSC][4];
 #pragma unroll
-        for (int s0 = 0; s0 < nsteps; s0 += 2) {
-            u32x4 A[2][4];
-            float4 X0[2][4], X1[2][4];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bool sok = s0 + u < nsteps;
+            for (int st = 0; st < NSC; ++st)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    A[u][g] = (sok && band_ok) ? ld16(arow + (size_t)16 * g * ld + 32 * (s0 + u)) : zero;
+                    A[st][g] = band_ok ? ld16(arow + (size_t)16 * g * ld + c0 + 32 * st) : zero;
+            if (c0 == 0) stage();
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    const bool ok = sok && tt < NT && hok[tt];
-                    const float4* hp = reinterpret_cast<const float4*>(hrow[tt] + 32 * (s0 + u));
-                    X0[u][tt] = ok ? hp[0] : float4{0, 0, 0, 0};
-                    X1[u][tt] = ok ? hp[1] : float4{0, 0, 0, 0};
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                if (s0 + u >= nsteps) break;
+            for (int st = 0; st < NSC; ++st) {
+                const int col = c0 + 32 * st;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     if (tt < NT) {
-                        u32x4 bh, bl;
-                        split_bf16x8(X0[u][tt], X1[u][tt], bh, bl);
+                        const int j = tt * 16 + tl;
+                        u32x4 bh = zero, bl = zero;
+                        if (j < T) {
+                            if (h_lds) {
+                                const size_t pe = ((size_t)j * I + col + 8 * kq) / 2;
+                                bh = *reinterpret_cast<const u32x4*>(s_hh + pe);
+                                bl = *reinterpret_cast<const u32x4*>(s_hl + pe);
+                            } else {
+                                const float4* hp = reinterpret_cast<const float4*>(hrow[tt] + col);
+                                split_bf16x8(hp[0], hp[1], bh, bl);
+                            }
+                        }
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            const bf16x8 Aw = __builtin_bit_cast(bf16x8, A[u][g]);
-                            acc[g][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aw, __builtin_bit_cast(bf16x8, bh),
-                                                                                 acc[g][tt], 0, 0, 0);
-                            acc[g][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aw, __builtin_bit_cast(bf16x8, bl),
-                                                                                 acc[g][tt], 0, 0, 0);
+                            const bf16x8 Aw = __builtin_bit_cast(bf16x8, A[st][g]);
+                            acc[g][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                Aw, __builtin_bit_cast(bf16x8, bh), acc[g][tt], 0, 0, 0);
+                            acc[g][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                Aw, __builtin_bit_cast(bf16x8, bl), acc[g][tt], 0, 0, 0);
                         }
                     }
                 }
@@ -347,7 +366,6 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
             }
         }
     }
-
 }
 
 // out[t][r] = bf16( sum_j w[t][j] * part[t*k+j][r] + sum_sb part_s[sb][t][r] (+ x) ),
@@ -524,12 +542,16 @@ KernelPick pick_combine(const DownXArgs& a) {
 }
 
 KernelPick pick_down_x(const DownXArgs& a) {
+    // four 16-byte units per lane per row where I allows (short reductions),
+    // 64 lanes per row from I = 2048
     const int ur = a.I / 8;
     const void* f;
 #define MOE_DX(LPR, NQ) f = MOE_FN((down_x_kernel<LPR, NQ>));
-    if (ur == 8) MOE_DX(8, 1)
-    else if (ur == 16) MOE_DX(16, 1)
-    else if (ur == 32) MOE_DX(32, 1)
+    if (ur == 8) MOE_DX(2, 4)
+    else if (ur == 16) MOE_DX(4, 4)
+    else if (ur == 32) MOE_DX(8, 4)
+    else if (ur == 64) MOE_DX(16, 4)
+    else if (ur == 128) MOE_DX(32, 4)
     else {
         switch (ur / 64) {
             case 1: MOE_DX(64, 1) break;
@@ -544,7 +566,7 @@ KernelPick pick_down_x(const DownXArgs& a) {
     }
 #undef MOE_DX
     const int grid = (a.max_act + a.nsh) * ((a.H + kDownXRows - 1) / kDownXRows);
-    return {f, dim3(grid), dim3(256), (size_t)a.gemv_max_tokens * a.I * 4};
+    return {f, dim3(grid), dim3(256), (size_t)kDownXLds};
 }
 
 template <int TB>
