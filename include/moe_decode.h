@@ -79,9 +79,17 @@ typedef struct moe_decode_config {
                                 second queue); 1: on the plan's second stream,
                                 forked before the router and joined before the down
                                 projection                                           */
-    int32_t topk_launch;     /* batch <= 4 only.  0: default; 1: top-k and bucketing
-                                in the router launch's last workgroup to arrive;
-                                2: in a launch of their own after the router         */
+    int32_t topk_launch;     /* batch <= 4 only.  0: default (3 where it applies,
+                                else 1); 1: top-k and bucketing in the router
+                                launch's last workgroup to arrive; 2: in a launch of
+                                their own after the router; 3: in every routed
+                                gate/up workgroup, each deriving the same work lists
+                                from the logits (no hand-off between workgroups),
+                                with the shared expert's gate/up in the same launch.
+                                3 runs every gate/up tile as a GEMV tile: with the
+                                default mfma_min_tokens that is what it does; a
+                                mfma_min_tokens <= batch keeps 0 at 1, and asking
+                                for 3 with it fails with MOE_ERR_UNSUPPORTED        */
     int32_t single_launch;   /* 0 (default) or 1: the staged launches.  2: the whole
                                 layer as ONE persistent launch -- possible when
                                 batch <= 4, shared_stream = 0, topk_launch != 2 and
@@ -110,6 +118,8 @@ typedef struct moe_decode_info {
     int32_t router_mfma;      /* 1: router is a split-K MFMA launch + a top-k launch     */
     int32_t single_launch;    /* 1: the layer runs as one persistent launch             */
     int32_t layer_grid;       /* its workgroup count (0 until the first forward)        */
+    int32_t topk_launch;      /* resolved top-k placement: 1, 2 or 3 (see the config),
+                                 0 with the single launch                              */
     size_t workspace_bytes;   /* device workspace owned by the plan                     */
 } moe_decode_info;
 

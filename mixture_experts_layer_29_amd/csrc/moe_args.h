@@ -147,6 +147,18 @@ struct FrontArgs {
     int32_t shared_blocks;  // workgroups [router_blocks, +shared_blocks) run the shared gate/up
 };
 
+// Gate/up launch that selects for itself (batch <= 4; the front launch before
+// it writes the logits z with the bias added and the shared expert's h):
+// every workgroup reads z, selects the top-k of all B tokens (one wave per
+// token) and buckets the pairs in LDS, then runs the tile of the active
+// expert its index maps to.  Workgroup 0 also writes the routing rows and the
+// work lists for the down launch and the caller.  Every workgroup computes the
+// same lists, so there is no hand-off inside the launch.
+struct SelGateUpArgs {
+    RouterArgs r;           // logits (r.z) and the routing / work-list outputs
+    GateUpArgs g;           // routed experts
+};
+
 // Whole layer in one launch (batch <= 4): tasks in dependency order
 // [router rows][shared gate/up][shared down][routed gate/up][routed down];
 // the first two groups are assigned by block index, the rest claimed in order.
@@ -188,6 +200,12 @@ KernelPick pick_init(const InitArgs& a);
 KernelPick pick_front(const FrontArgs& f, bool small_router, bool select_in_router, int shared_tb);
 int front_router_blocks(const RouterArgs& a, bool small_router);
 KernelPick pick_topk(const RouterArgs& a);
+// Front launch of the select-in-gate/up form (batch <= 4): f.router_blocks
+// (= E) router rows, then f.shared_blocks (= Is or 0) shared gate/up row
+// pairs, one per workgroup, K split over its four waves.
+KernelPick pick_front_split(const FrontArgs& f);
+// Gate/up launch that selects for itself (batch <= 4).
+KernelPick pick_gateup_select(const SelGateUpArgs& a, int max_entries);
 KernelPick pick_gateup(const GateUpArgs& a, int max_entries, int gemv_tokens);
 constexpr int kDownXRows = 256;           // output rows per expert-major down tile
 constexpr int kDownXLds = 64 * 1024;      // LDS for a down tile's staged h rows

@@ -5,8 +5,8 @@
 // article describes in Part 1 section 1) and sizes the workspace; it touches
 // no device.  The first forward allocates the workspace, a second stream and
 // events, and builds a HIP graph: front (router, and by default the shared
-// expert's gate/up in trailing workgroups) -> [top-k] -> routed gate/up ->
-// down.  With shared_stream = 1 the shared expert's gate/up is a parallel
+// expert's gate/up in trailing workgroups) -> [top-k] -> routed gate/up (at
+// batch <= 4 by default selecting for itself) -> down.  With shared_stream = 1 the shared expert's gate/up is a parallel
 // branch on the second stream joined before the down projection instead
 // (article Part 1 section 3: shared expert on its own stream, overlapped with
 // routing; "What's next": per-step host work replayed as a graph).  Later
@@ -87,6 +87,7 @@ struct moe_decode_plan_s {
     bool small_router;    // batch <= 4: one router launch; else MFMA router + top-k launch
     bool shared_stream;   // shared gate/up on the second stream instead of the front launch
     bool select_in_router;// batch <= 4: top-k + bucketing in the router's last workgroup
+    bool select_in_gateup;// batch <= 4: every routed gate/up workgroup selects and buckets
     bool fused;           // the whole layer as one persistent launch
     bool expert_major;    // staged down: expert-major tiles + combine launch (else output-stationary)
     size_t layer_lds;     // its dynamic LDS bytes
@@ -105,6 +106,7 @@ struct moe_decode_plan_s {
     RouterArgs& ra = fa.r;
     GateUpArgs& gs = fa.s;
     GateUpArgs ga{};
+    SelGateUpArgs sga{};  // gate/up launch of the select-in-gate/up form
     DownArgs da{};     // down of the single launch
     DownXArgs dx{};    // down of the staged launches
     LayerArgs la{};
@@ -128,6 +130,10 @@ struct moe_decode_plan_s {
 namespace {
 
 bool has_shared(const moe_decode_plan_s* p) { return p->cfg.shared_inter > 0; }
+// top-k and bucketing in a launch of their own (batch > 4, or topk_launch = 2)
+bool topk_own_launch(const moe_decode_plan_s* p) { return !p->select_in_router && !p->select_in_gateup; }
+// the shared expert's gate/up in trailing workgroups of the front launch
+bool shared_in_front(const moe_decode_plan_s* p) { return has_shared(p) && !p->shared_stream; }
 
 moe_status validate(const moe_decode_config* c) {
     if (!c) return fail(MOE_ERR_INVALID, "config is NULL");
@@ -150,8 +156,8 @@ moe_status validate(const moe_decode_config* c) {
         return fail(MOE_ERR_INVALID, "mfma_min_tokens must be >= 0");
     if (c->shared_stream != 0 && c->shared_stream != 1)
         return fail(MOE_ERR_INVALID, "shared_stream must be 0 or 1");
-    if (c->topk_launch < 0 || c->topk_launch > 2)
-        return fail(MOE_ERR_INVALID, "topk_launch must be 0, 1 or 2");
+    if (c->topk_launch < 0 || c->topk_launch > 3)
+        return fail(MOE_ERR_INVALID, "topk_launch must be 0, 1, 2 or 3");
     if (c->single_launch < 0 || c->single_launch > 2)
         return fail(MOE_ERR_INVALID, "single_launch must be 0, 1 or 2");
     if (c->router_bias && (reinterpret_cast<uintptr_t>(c->router_bias) & 3))
@@ -283,9 +289,10 @@ void fill_static_args(moe_decode_plan_s* p) {
         s.kslice = p->kslice;
     }
 
-    p->fa.router_blocks = front_router_blocks(r, p->small_router);
-    p->fa.shared_blocks = (has_shared(p) && !p->shared_stream)
-                              ? c.shared_inter / kPairsPerGemvTile : 0;
+    // the select-in-gate/up form's front: one router row / shared row pair per workgroup
+    p->fa.router_blocks = p->select_in_gateup ? c.n_experts : front_router_blocks(r, p->small_router);
+    p->fa.shared_blocks = !shared_in_front(p) ? 0
+                          : p->select_in_gateup ? c.shared_inter : c.shared_inter / kPairsPerGemvTile;
 
     DownArgs& d = p->da;
     d.n_act = g.n_act;
@@ -364,9 +371,16 @@ void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, con
     p->dx.w2 = p->da.w2;
     p->dx.s2 = p->da.s2;
     p->dx.out = p->da.out;
-    p->kf = pick_front(p->fa, p->small_router, p->select_in_router, p->shared_mfma ? 0 : c.batch);
-    if (!p->select_in_router) p->kt = pick_topk(p->ra);
-    p->kg = pick_gateup(p->ga, p->max_act, p->routed_gemv_tb);
+    if (p->select_in_gateup) {
+        p->sga.r = p->ra;
+        p->sga.g = p->ga;
+        p->kf = pick_front_split(p->fa);
+        p->kg = pick_gateup_select(p->sga, p->max_act);
+    } else {
+        p->kf = pick_front(p->fa, p->small_router, p->select_in_router, p->shared_mfma ? 0 : c.batch);
+        if (topk_own_launch(p)) p->kt = pick_topk(p->ra);
+        p->kg = pick_gateup(p->ga, p->max_act, p->routed_gemv_tb);
+    }
     if (has_shared(p) && p->shared_stream) p->ks = pick_gateup(p->gs, 1, p->shared_mfma ? 1 : c.batch);
     if (p->expert_major) {
         p->kd = pick_down_x(p->dx);
@@ -428,6 +442,8 @@ moe_status device_init(moe_decode_plan_s* p, hipStream_t stream) {
     return MOE_OK;
 }
 
+void* gateup_args(moe_decode_plan_s* p) { return p->select_in_gateup ? (void*)&p->sga : (void*)&p->ga; }
+
 moe_status launch(const KernelPick& k, void* args, hipStream_t s) {
     void* a[] = {args};
     HIP_TRY(hipLaunchKernel(k.func, k.grid, k.block, a, k.lds, s));
@@ -456,13 +472,13 @@ moe_status enqueue_eager(moe_decode_plan_s* p, hipStream_t stream, hipEvent_t* e
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT], stream));
     if ((st = launch(p->kf, &p->fa, stream))) return st;
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT + 1], stream));
-    if (!p->select_in_router) {
+    if (topk_own_launch(p)) {
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_TOPK], stream));
         if ((st = launch(p->kt, &p->ra, stream))) return st;
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_TOPK + 1], stream));
     }
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_GATEUP], stream));
-    if ((st = launch(p->kg, &p->ga, stream))) return st;
+    if ((st = launch(p->kg, gateup_args(p), stream))) return st;
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_GATEUP + 1], stream));
     if (side) HIP_TRY(hipStreamWaitEvent(stream, p->ev_join, 0));
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_DOWN], stream));
@@ -498,14 +514,14 @@ moe_status build_graph(moe_decode_plan_s* p) {
     }
     void* af[] = {&p->fa};
     void* ar[] = {&p->ra};
-    void* ag[] = {&p->ga};
+    void* ag[] = {gateup_args(p)};
     void* as[] = {&p->gs};
     void* ad[] = {p->expert_major ? (void*)&p->dx : (void*)&p->da};
     void* ac[] = {&p->dx};
     hipKernelNodeParams np = node_params(p->kf, af);
     HIP_TRY(hipGraphAddKernelNode(&p->n_front, p->graph, nullptr, 0, &np));
     hipGraphNode_t route_done = p->n_front;
-    if (!p->select_in_router) {
+    if (topk_own_launch(p)) {
         np = node_params(p->kt, ar);
         HIP_TRY(hipGraphAddKernelNode(&p->n_topk, p->graph, &p->n_front, 1, &np));
         route_done = p->n_topk;
@@ -538,13 +554,13 @@ moe_status patch_graph(moe_decode_plan_s* p) {
     }
     void* af[] = {&p->fa};
     void* ar[] = {&p->ra};
-    void* ag[] = {&p->ga};
+    void* ag[] = {gateup_args(p)};
     void* as[] = {&p->gs};
     void* ad[] = {p->expert_major ? (void*)&p->dx : (void*)&p->da};
     void* ac[] = {&p->dx};
     hipKernelNodeParams np = node_params(p->kf, af);
     HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_front, &np));
-    if (!p->select_in_router) {
+    if (topk_own_launch(p)) {
         np = node_params(p->kt, ar);
         HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_topk, &np));
     }
@@ -628,7 +644,7 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
         else if (h_lds > kLayerLds) why = "the h rows exceed the LDS budget";
         else if (!shape_ok) why = "no down shape for this inter";
         else if (c.shared_stream) why = "shared_stream = 1 asks for the staged launches";
-        else if (c.topk_launch == 2) why = "topk_launch = 2 asks for the staged launches";
+        else if (c.topk_launch == 2 || c.topk_launch == 3) why = "topk_launch = 2 or 3 asks for the staged launches";
         // measured slower than the staged launches on MI355X (one workgroup per
         // CU and a latency-inflated critical path), so only on request
         p->fused = c.single_launch == 2 && !why;
@@ -637,6 +653,29 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
             delete p;
             return fail(MOE_ERR_UNSUPPORTED, "single_launch = 2: %s", why);
         }
+    }
+    // Batch <= 4: the selection by default runs in every routed gate/up
+    // workgroup (topk_launch 3).  That form runs every tile as a GEMV tile, so
+    // with the library's MFMA threshold it turns MFMA tiles off; a threshold
+    // the caller set that could reach MFMA tiles keeps the selection in the
+    // router's last workgroup (topk_launch 1) unless 3 is asked for.
+    p->select_in_gateup = false;
+    if (!p->fused && p->small_router && (c.topk_launch == 0 || c.topk_launch == 3)) {
+        const bool gemv_only = !p->shared_mfma && (p->mfma_min == 0 || p->mfma_min > c.batch);
+        if (gemv_only || c.mfma_min_tokens == 0) {
+            p->select_in_gateup = true;
+            p->mfma_min = 0;
+            p->shared_mfma = false;
+            p->routed_gemv_tb = c.batch;
+            p->select_in_router = false;
+        } else if (c.topk_launch == 3) {
+            delete p;
+            return fail(MOE_ERR_UNSUPPORTED, "topk_launch = 3 runs GEMV tiles only; mfma_min_tokens %d "
+                        "reaches MFMA tiles at batch %d", c.mfma_min_tokens, c.batch);
+        }
+    } else if (c.topk_launch == 3 && !p->fused) {
+        delete p;
+        return fail(MOE_ERR_UNSUPPORTED, "topk_launch = 3 needs batch <= 4 with x in the LDS budget");
     }
     p->expert_major = c.batch > kDownOsMaxBatch;
     p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K, p->fused, p->expert_major);
@@ -736,8 +775,9 @@ moe_status moe_decode_plan_info(moe_decode_plan_t p, moe_decode_info* info) {
     if (!p || !info) return fail(MOE_ERR_INVALID, "NULL argument");
     info->variant = p->variant;
     info->n_kernels = p->fused ? 1
-                      : 3 + (p->select_in_router ? 0 : 1) + (has_shared(p) && p->shared_stream ? 1 : 0) +
+                      : 3 + (topk_own_launch(p) ? 1 : 0) + (has_shared(p) && p->shared_stream ? 1 : 0) +
                             (p->expert_major ? 1 : 0);
+    info->topk_launch = p->fused ? 0 : p->select_in_gateup ? 3 : p->select_in_router ? 1 : 2;
     info->mfma_min_tokens = p->mfma_min;
     info->shared_mfma = p->shared_mfma ? 1 : 0;
     info->shared_stream = p->shared_stream ? 1 : 0;
@@ -777,7 +817,7 @@ moe_status moe_decode_profile_read(moe_decode_plan_t p, int32_t cap, double* tot
         for (int s = 0; s < S_COUNT && s < cap; ++s) {
             const bool used = p->fused ? s == S_LAYER
                               : !((s == S_SHARED && !(has_shared(p) && p->shared_stream)) ||
-                                  (s == S_TOPK && p->select_in_router) || s == S_LAYER ||
+                                  (s == S_TOPK && !topk_own_launch(p)) || s == S_LAYER ||
                                   (s == S_COMBINE && !p->expert_major));
             if (!used) continue;
             hipEvent_t a = p->prof_events[((size_t)f * S_COUNT + s) * 2];

@@ -252,64 +252,71 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 constexpr int kNone = 0x7fffffff;
 
 // Unsigned key with the order of the float (larger key = larger value; every
-// key of a number, -inf included, is > 0).  -0 and +0 get different keys, so
-// they are compared through the floats where that matters.
+// key of a number, -inf included, is > 0).  -0 and +0 get different keys;
+// adding +0.0f first folds -0 into +0.
 __device__ __forceinline__ uint32_t order_key(float v) {
     const uint32_t u = __float_as_uint(v);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // Top-k of one token by one wave.  Slot m of lane l holds the logit of expert
-// m * 64 + l in v[m] (slots at or past E are never selected).  Each round
-// takes the wave-wide largest remaining logit (DPP max over the lanes' current
-// best); equal logits go to the lower expert id (ballot; DPP min when several
-// lanes tie); the winning lane then drops that slot and finds its next best.
-// Lane r < k ends with entry r of the selection (my_e, my_z); the round loop
-// is not unrolled, so its code stays small (the selection runs once per
-// launch, from a cold instruction cache).
+// m * 64 + l in v[m] (slots at or past E are never selected).  Each lane
+// first sorts its slots (Batcher's odd-even merge network) by the 64-bit key
+// (order key of the logit, then the complement of the expert id), so larger
+// logits come first and equal logits go to the lower id; -0 is keyed as +0.
+// Each round then takes the wave-wide largest head (DPP max over the upper
+// halves; a second max over the lower halves only when several lanes hold
+// that logit), and the winning lane pops its head.  Lane r < k ends with
+// entry r of the selection (my_e, my_z).  A round costs one reduction and a
+// register shift, no rescan of the slots, and the round loop is not unrolled,
+// so the code stays small (it runs once per launch, from a cold instruction
+// cache).
 template <int NS>
 __device__ __forceinline__ void topk_wave(const float (&v)[NS], int E, int k, int lane, int& my_e, float& my_z) {
-    uint32_t avail = 0;
+    uint64_t K[NS];  // 0 = empty slot
 #pragma unroll
-    for (int m = 0; m < NS; ++m)
-        if (m * 64 + lane < E) avail |= 1u << m;
-    float bv;      // lane's best remaining logit
-    uint32_t bk;   // its order key, 0 when the lane has nothing left
-    int be;        // its expert id
-    auto lane_best = [&]() {
-        bv = -INFINITY;
-        bk = 0;
-        be = kNone;
+    for (int m = 0; m < NS; ++m) {
+        const int e = m * 64 + lane;
+        const uint64_t key = ((uint64_t)order_key(v[m] + 0.0f) << 32) | (uint32_t)~e;
+        K[m] = e < E ? key : 0ull;
+    }
 #pragma unroll
-        for (int m = 0; m < NS; ++m) {
-            const uint32_t km = order_key(v[m]);
-            const bool take = ((avail >> m) & 1u) && km > bk;  // strict: ties keep the lower id
-            bv = take ? v[m] : bv;
-            bk = take ? km : bk;
-            be = take ? m * 64 + lane : be;
-        }
-    };
-    lane_best();
+    for (int p = 1; p < NS; p <<= 1)
+#pragma unroll
+        for (int d = p; d >= 1; d >>= 1)
+#pragma unroll
+            for (int j = d % p; j + d < NS; j += 2 * d)
+#pragma unroll
+                for (int i = 0; i < d && i + j + d < NS; ++i)
+                    if ((i + j) / (2 * p) == (i + j + d) / (2 * p)) {
+                        const uint64_t x = K[i + j], y = K[i + j + d];
+                        const bool sw = y > x;
+                        K[i + j] = sw ? y : x;
+                        K[i + j + d] = sw ? x : y;
+                    }
     my_e = -1;
     my_z = -INFINITY;
 #pragma unroll 1
     for (int r = 0; r < k; ++r) {
-        const uint32_t mk = wave_max_u32(bk);
+        const uint32_t hk = (uint32_t)(K[0] >> 32);
+        const uint32_t mk = wave_max_u32(hk);
         if (mk == 0) break;
-        // lanes holding the largest logit (the float compare also ties -0 with +0)
-        const float m = __uint_as_float((mk & 0x80000000u) ? (mk & 0x7fffffffu) : ~mk);
-        const unsigned long long bal = __ballot(bk != 0 && bv == m);
-        int e;
-        if (__popcll(bal) == 1) e = __builtin_amdgcn_readlane(be, __ffsll(bal) - 1);
-        else e = (int)~wave_max_u32(((bal >> lane) & 1ull) ? ~(uint32_t)be : 0u);
-        const float ez = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), e & 63));
+        unsigned long long bal = __ballot(hk == mk);
+        if (__popcll(bal) != 1) {  // the same logit in several lanes: the lowest id
+            const uint32_t lo = (uint32_t)K[0];
+            const uint32_t ml = wave_max_u32(hk == mk ? lo : 0u);
+            bal = __ballot(hk == mk && lo == ml);
+        }
+        const int w = __ffsll(bal) - 1;
+        const int e = ~__builtin_amdgcn_readlane((int)(uint32_t)K[0], w);
         if (lane == r) {
             my_e = e;
-            my_z = ez;
+            my_z = __uint_as_float((mk & 0x80000000u) ? (mk & 0x7fffffffu) : ~mk);
         }
-        if (be == e) {  // the winner drops the slot and takes its next best
-            avail &= ~(1u << (e >> 6));
-            lane_best();
+        if (lane == w) {
+#pragma unroll
+            for (int m = 0; m + 1 < NS; ++m) K[m] = K[m + 1];
+            K[NS - 1] = 0ull;
         }
     }
 }
@@ -317,11 +324,11 @@ __device__ __forceinline__ void topk_wave(const float (&v)[NS], int E, int k, in
 // Routing weights of the selected logits (softmax or sigmoid, optional
 // renormalisation over the selection, times routed_scale).  Lane r < k holds
 // entry r of the selection (expert er, logit zr); zmax is the largest
-// selected logit.  Writes the token's topk_idx / topk_w row (and s_pair_e
-// when given).  zrow (the token's logits, readable by this wave) is read only
+// selected logit.  Writes the token's topk_idx / topk_w row (unless
+// !to_global) and its s_pair_e row when given.  zrow (the token's logits, readable by this wave) is read only
 // for a softmax without renormalisation, whose denominator runs over all E.
 __device__ __forceinline__ void route_one(const RouterArgs& a, int t, int lane, const float* zrow, int er, float zr,
-                                          float zmax, int32_t* s_pair_e) {
+                                          float zmax, int32_t* s_pair_e, bool to_global = true) {
     const int k = a.k, E = a.E;
     const bool mine = lane < k;
     float w;
@@ -341,8 +348,10 @@ __device__ __forceinline__ void route_one(const RouterArgs& a, int t, int lane, 
         w = a.renormalize ? sg / wave_sum(sg) : sg;
     }
     if (mine) {
-        st_dev(a.topk_idx + t * k + lane, er);
-        st_dev(a.topk_w + t * k + lane, w * a.routed_scale);
+        if (to_global) {
+            st_dev(a.topk_idx + t * k + lane, er);
+            st_dev(a.topk_w + t * k + lane, w * a.routed_scale);
+        }
         if (s_pair_e) s_pair_e[t * k + lane] = er;
     }
 }
@@ -358,10 +367,35 @@ __device__ __forceinline__ void bucket_meta(const RouterArgs& a, int nact, int n
     st_dev(a.meta + M_ROUTER_CNT, 0);  // re-armed for the next launch
 }
 
-// Bucketing by one wave for B*k <= 64 pairs (pair p in lane p): a pair's slot
-// is the number of pairs with a smaller (expert, pair) key, so slots are
-// ordered by expert then token; the first pair of each expert defines the
-// active-expert entry.  No barriers and no LDS atomics.
+// Slot of pair `lane` (expert e) among np <= 64 pairs held one per lane: the
+// number of pairs with a smaller (expert, pair) key, so slots are ordered by
+// expert then token.  The first pair of each expert leads; entries (active
+// experts) are numbered in expert order (apos) and an entry's slots start at
+// its lead's slot.  cnt: the expert's pair count.
+struct PairSlot {
+    int pos, apos, cnt;
+    bool lead;
+};
+__device__ __forceinline__ PairSlot pair_slot(int e, int np, int lane) {
+    PairSlot r{0, 0, 0, false};
+    bool first = true;
+    for (int q = 0; q < np; ++q) {
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        r.pos += (eq < e || (eq == e && q < lane)) ? 1 : 0;
+        r.cnt += eq == e ? 1 : 0;
+        if (eq == e && q < lane) first = false;
+    }
+    r.lead = lane < np && first;
+    const unsigned long long fm = __ballot(r.lead);
+    for (int q = 0; q < np; ++q) {
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        r.apos += (((fm >> q) & 1ull) && eq < e) ? 1 : 0;
+    }
+    return r;
+}
+
+// Bucketing by one wave for B*k <= 64 pairs (pair p in lane p) into the
+// global work lists (see pair_slot).  No barriers and no LDS atomics.
 __device__ __forceinline__ void bucket_wave(const RouterArgs& a, const int32_t* s_pair_e, int lane) {
     const int np = a.B * a.k;
     const int e = lane < np ? s_pair_e[lane] : kNone;
@@ -369,28 +403,14 @@ __device__ __forceinline__ void bucket_wave(const RouterArgs& a, const int32_t* 
         if (lane == 0) bucket_meta(a, 0, 0, np, -1);
         return;
     }
-    int pos = 0, cnt = 0;
-    bool first = true;
-    for (int q = 0; q < np; ++q) {
-        const int eq = __builtin_amdgcn_readlane(e, q);
-        pos += (eq < e || (eq == e && q < lane)) ? 1 : 0;
-        cnt += eq == e ? 1 : 0;
-        if (eq == e && q < lane) first = false;
+    const PairSlot ps = pair_slot(e, np, lane);
+    if (lane < np) st_dev(a.perm + ps.pos, lane);
+    if (ps.lead) {
+        st_dev(a.act_e + ps.apos, e);
+        st_dev(a.act_off + ps.apos, ps.pos);
     }
-    if (lane < np) st_dev(a.perm + pos, lane);
-    const bool lead = lane < np && first;
-    const unsigned long long fm = __ballot(lead);
-    int apos = 0;
-    for (int q = 0; q < np; ++q) {
-        const int eq = __builtin_amdgcn_readlane(e, q);
-        apos += (((fm >> q) & 1ull) && eq < e) ? 1 : 0;
-    }
-    if (lead) {
-        st_dev(a.act_e + apos, e);
-        st_dev(a.act_off + apos, pos);
-    }
-    const int nact = __popcll(fm);
-    const int nmfma = __popcll(__ballot(lead && a.mfma_min_tokens > 0 && cnt >= a.mfma_min_tokens));
+    const int nact = __popcll(__ballot(ps.lead));
+    const int nmfma = __popcll(__ballot(ps.lead && a.mfma_min_tokens > 0 && ps.cnt >= a.mfma_min_tokens));
     if (lane == 0) bucket_meta(a, nact, nmfma, np, np);
 }
 
@@ -468,10 +488,12 @@ __device__ __forceinline__ void bucket_block(const RouterArgs& a, const int32_t*
 // src: per-token logit rows (E floats); with `from_acc` they are split-K
 // accumulators: the bias is added, the sum stored to a.z and the accumulator
 // cleared.  Ends with a workgroup barrier, after which s_pair_e (if given)
-// holds the selected ids of the workgroup's tokens.
-template <int NS>
+// holds the selected ids of the workgroup's tokens.  !to_global: the routing
+// rows (topk_idx / topk_w) are not written.  COH: src was written by other
+// workgroups of this launch (coherent loads); else by an earlier launch.
+template <int NS, bool COH = true>
 __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float* src, const float* bias,
-                                              bool from_acc, int32_t* s_pair_e) {
+                                              bool from_acc, int32_t* s_pair_e, bool to_global = true) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = a.E, B = a.B, k = a.k;
     const int t = t0 + wave;
@@ -484,7 +506,8 @@ __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float
             const int e = m * 64 + lane;
             float x = -INFINITY;
             if (e < E) {
-                x = ld_dev(row + e);
+                if constexpr (COH) x = ld_dev(row + e);
+                else x = row[e];
                 if (from_acc) {
                     x += bias ? bias[e] : 0.0f;
                     st_dev(zo + e, x);
@@ -499,7 +522,7 @@ __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float
         // a full softmax reads the token's logits back: from_acc rows are in a.z (this
         // wave's stores, complete after the wait)
         __builtin_amdgcn_s_waitcnt(0);
-        route_one(a, t, lane, from_acc ? zo : row, my_e, my_z, __shfl(my_z, 0, 64), s_pair_e);
+        route_one(a, t, lane, from_acc ? zo : row, my_e, my_z, __shfl(my_z, 0, 64), s_pair_e, to_global);
     }
     __syncthreads();
 }
@@ -511,7 +534,7 @@ __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float
 
 template <int TB, bool COH = false>
 __device__ __forceinline__ void gemv_gateup_tile(const GateUpArgs& a, const uint16_t* W, int off, int T, int local,
-                                 uint16_t* s_x);
+                                 uint16_t* s_x, const int32_t* s_tok = nullptr);
 template <int NTM>
 __device__ __forceinline__ bool mfma_gateup_tile(const GateUpArgs& a, const uint16_t* W, int entry, int off, int T, int local);
 
@@ -651,10 +674,11 @@ __device__ __forceinline__ void router_mfma_tile(const RouterArgs& a, int tile) 
 
 // Full-K GEMV tile: wave w computes row pair i = 4*local + w (gate row i and
 // up row n+i) for the entry's T <= TB tokens, whose activations the workgroup
-// stages in LDS after issuing its weight loads.
+// stages in LDS after issuing its weight loads.  s_tok (TB <= 4, not COH): the
+// entry's token ids in LDS, in slot order, instead of a.perm.
 template <int TB, bool COH>
 __device__ __forceinline__ void gemv_gateup_tile(const GateUpArgs& a, const uint16_t* W, int off, int T, int local,
-                                 uint16_t* s_x) {
+                                 uint16_t* s_x, const int32_t* s_tok) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = a.H, n = a.n, units = H >> 3, nu = (units + 63) >> 6;
     const int i = local * kPairsPerGemvTile + wave;
@@ -671,7 +695,8 @@ __device__ __forceinline__ void gemv_gateup_tile(const GateUpArgs& a, const uint
     int tk[4] = {0, 0, 0, 0};
     if constexpr (!COH && TB <= 4) {
 #pragma unroll
-        for (int j = 0; j < TB; ++j) tk[j] = j < T ? uni(a.perm[off + j]) / a.pair_div : 0;
+        for (int j = 0; j < TB; ++j)
+            tk[j] = j >= T ? 0 : s_tok ? uni(s_tok[j]) : uni(a.perm[off + j]) / a.pair_div;
     }
     auto xsrc = [&](int idx) {  // unit idx of the staged [T][H] activations
         const int j = idx / units, uu = idx - j * units;

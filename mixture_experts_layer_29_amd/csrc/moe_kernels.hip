@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void topk_bucket_kernel(RouterArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int B = a.B, np = B * a.k;
     const bool single = gridDim.x == 1;
-    select_tokens<NS>(a, blockIdx.x * 4, a.zacc, a.bias, true, single ? s_pair_e : nullptr);
+    select_tokens<NS, false>(a, blockIdx.x * 4, a.zacc, a.bias, true, single ? s_pair_e : nullptr);
     if (!single) {
         if (!arrive_last(reinterpret_cast<unsigned*>(&a.meta[M_ROUTER_CNT]), gridDim.x, &s_flag)) return;
         for (int p = tid; p < np; p += 256) s_pair_e[p] = ld_dev(a.topk_idx + p);
@@ -131,6 +131,161 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// batch <= 4 with the selection in the gate/up launch: router_split writes
+// the logits, then every routed gate/up workgroup selects and buckets for
+// itself, so no workgroup waits on another's counter and the shared expert's
+// gate/up streams while the routed workgroups select
+// ---------------------------------------------------------------------------
+
+// Dot products of NR weight rows with the B <= TB token rows of x ([B][H]),
+// K split over the workgroup's 256 threads in interleaved 16-byte units (the
+// row loads are coalesced across the workgroup; x is a few KB per token and
+// stays in L2).  The wave sums meet in s_part in a fixed order; every thread
+// returns the totals.
+template <int TB, int NR>
+__device__ __forceinline__ void wg_rows_dot(const uint16_t* const (&w)[NR], const uint16_t* x, int H, int B,
+                                            float (*s_part)[NR][TB], float (&res)[NR][TB]) {
+    constexpr int Q = 4;  // units per thread in flight
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int units = H >> 3;
+    const u32x4 zero = u32x4{0, 0, 0, 0};
+    float acc[NR][TB];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < TB; ++t) acc[r][t] = 0.0f;
+    for (int u0 = 0; u0 < units; u0 += 256 * Q) {
+        u32x4 wv[Q][NR], xv[Q][TB];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int u = u0 + 256 * q + tid;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) wv[q][r] = u < units ? ld16(w[r] + u * 8) : zero;
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int u = u0 + 256 * q + tid;
+#pragma unroll
+            for (int t = 0; t < TB; ++t) xv[q][t] = (u < units && t < B) ? ld16(x + (size_t)t * H + u * 8) : zero;
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int t = 0; t < TB; ++t)
+                    if (t < B) acc[r][t] = dot8(wv[q][r], xv[q][t], acc[r][t]);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            if (t < B) {
+                const float sum = wave_sum(acc[r][t]);
+                if (lane == 0) s_part[wave][r][t] = sum;
+            }
+        }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+            res[r][t] = (s_part[0][r][t] + s_part[1][r][t]) + (s_part[2][r][t] + s_part[3][r][t]);
+}
+
+// Front launch of the select-in-gate/up form (batch <= 4): workgroups
+// [0, router_blocks = E) compute one router row each (z = x . Wr[e] + bias);
+// workgroups [E, E + shared_blocks) one gate/up row pair of the shared expert
+// each (hs = SiLU(gate) * up).  Small workgroups, all resident at once: the
+// launch is one round trip of weight loads wide.
+template <int TB>
+__global__ __launch_bounds__(256) void front_split_kernel(FrontArgs f) {
+    const RouterArgs& a = f.r;
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x < f.router_blocks) {
+        __shared__ float s_part[4][1][TB];
+        const int e = blockIdx.x;
+        const uint16_t* w[1] = {a.wr + (size_t)e * a.H};
+        float z[1][TB];
+        wg_rows_dot<TB, 1>(w, a.x, a.H, a.B, s_part, z);
+        const float b = a.bias ? a.bias[e] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+            if (tid == t && t < a.B) a.z[(size_t)t * a.E + e] = z[0][t] + b;
+    } else {
+        __shared__ float s_part[4][2][TB];
+        const GateUpArgs& s = f.s;
+        const int i = blockIdx.x - f.router_blocks;
+        const uint16_t* w[2] = {s.w + (size_t)i * s.H, s.w + (size_t)(s.n + i) * s.H};
+        float gu[2][TB];
+        wg_rows_dot<TB, 2>(w, s.x, s.H, a.B, s_part, gu);
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+            if (tid == t && t < a.B) s.h[(size_t)t * s.n + i] = silu_f(gu[0][t]) * gu[1][t];
+    }
+}
+
+// Wave t < B selects token t's experts from z (the routing rows are written
+// by workgroup 0 only), wave 0 buckets the B*k pairs into LDS lists (and, in
+// workgroup 0, into the global lists the down launch reads), then the
+// workgroup runs tile `local` of entry `entry` with the entry's token ids from
+// LDS.  Every workgroup derives the same lists from the same logits.  At
+// B = 1 the k experts are distinct, so pair j is entry j in slot j.
+template <int TB, int NS>
+__global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
+    extern __shared__ __align__(16) uint16_t s_x[];  // [B][H]
+    __shared__ int32_t s_pair_e[4 * kMaxTopK];
+    __shared__ int32_t s_tok[4 * kMaxTopK];  // slot -> token
+    __shared__ int32_t s_act_e[4 * kMaxTopK];
+    __shared__ int32_t s_act_off[4 * kMaxTopK + 1];
+    __shared__ int32_t s_nact;
+    const RouterArgs& a = sa.r;
+    const GateUpArgs& g = sa.g;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int b = blockIdx.x;
+    const bool out = b == 0;
+    select_tokens<NS, false>(a, 0, a.z, nullptr, false, s_pair_e, out);
+    if (tid < 64) {
+        const int np = a.B * a.k;
+        const int e = lane < np ? s_pair_e[lane] : kNone;
+        int nact = 0;
+        if (__ballot(lane < np && (e < 0 || e >= a.E))) {  // never hand an invalid id to the experts
+            if (out && lane == 0) bucket_meta(a, 0, 0, np, -1);
+        } else {
+            const PairSlot ps = a.B == 1 ? PairSlot{lane, lane, 1, lane < np} : pair_slot(e, np, lane);
+            if (lane < np) s_tok[ps.pos] = lane / a.k;
+            if (ps.lead) {
+                s_act_e[ps.apos] = e;
+                s_act_off[ps.apos] = ps.pos;
+            }
+            nact = __popcll(__ballot(ps.lead));
+            if (out) {
+                if (lane < np) a.perm[ps.pos] = lane;
+                if (ps.lead) {
+                    a.act_e[ps.apos] = e;
+                    a.act_off[ps.apos] = ps.pos;
+                }
+                if (lane == 0) bucket_meta(a, nact, 0, np, np);
+            }
+        }
+        if (lane == 0) {
+            s_nact = nact;
+            s_act_off[nact] = np;
+        }
+    }
+    __syncthreads();
+    const int entry = b / g.tiles_per_expert, local = b % g.tiles_per_expert;
+    if (entry >= uni(s_nact)) return;
+    const int e = uni(s_act_e[entry]), off = uni(s_act_off[entry]);
+    const int T = uni(s_act_off[entry + 1]) - off;
+    if (T > TB) {  // an expert holds at most one pair per token, so T <= B <= TB
+        if (tid == 0 && local == 0) atomicOr(&g.meta[M_ERR], ERR_TILE);
+        return;
+    }
+    gemv_gateup_tile<TB>(g, g.w + (size_t)e * (size_t)g.expert_stride, off, T, local, s_x, s_tok + off);
+}
 
 // ---------------------------------------------------------------------------
 // down, output-stationary (staged launches, small batches): each workgroup
@@ -477,6 +632,30 @@ KernelPick pick_topk(const RouterArgs& a) {
         default: fn = MOE_FN(topk_bucket_kernel<16>); break;
     }
     return {fn, dim3((a.B + 3) / 4), dim3(256), 0};
+}
+
+KernelPick pick_front_split(const FrontArgs& f) {
+    const void* fn;
+    switch (tb_bucket(f.r.B)) {
+        case 1: fn = MOE_FN(front_split_kernel<1>); break;
+        case 2: fn = MOE_FN(front_split_kernel<2>); break;
+        default: fn = MOE_FN(front_split_kernel<4>); break;
+    }
+    return {fn, dim3(f.router_blocks + f.shared_blocks), dim3(256), 0};
+}
+
+KernelPick pick_gateup_select(const SelGateUpArgs& a, int max_entries) {
+    const int tb = tb_bucket(a.r.B), ns = tb_bucket((a.r.E + 63) / 64);
+    const void* f;
+    switch (tb * 32 + ns) {
+#define MOE_GS(TB, NS) case TB * 32 + NS: f = MOE_FN((gateup_select_kernel<TB, NS>)); break;
+#define MOE_GS_NS(TB) MOE_GS(TB, 1) MOE_GS(TB, 2) MOE_GS(TB, 4) MOE_GS(TB, 8) MOE_GS(TB, 16)
+        MOE_GS_NS(1) MOE_GS_NS(2) MOE_GS_NS(4)
+#undef MOE_GS_NS
+#undef MOE_GS
+        default: f = nullptr;
+    }
+    return {f, dim3(max_entries * a.g.tiles_per_expert), dim3(256), (size_t)a.r.B * a.r.H * 2};
 }
 
 // gemv_tokens: the largest token count a GEMV tile of this list may see.

@@ -67,7 +67,11 @@ def test_supported_configs_plan(kw):
     (dict(force_variant=3), moe.MOE_ERR_INVALID),
     (dict(mfma_min_tokens=-1), moe.MOE_ERR_INVALID),
     (dict(shared_stream=2), moe.MOE_ERR_INVALID),
-    (dict(topk_launch=3), moe.MOE_ERR_INVALID),
+    (dict(topk_launch=4), moe.MOE_ERR_INVALID),
+    (dict(topk_launch=-1), moe.MOE_ERR_INVALID),
+    (dict(batch=8, topk_launch=3), moe.MOE_ERR_UNSUPPORTED),
+    (dict(batch=4, topk_launch=3, mfma_min_tokens=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=16384, batch=4, topk_launch=3), moe.MOE_ERR_UNSUPPORTED),
     (dict(single_launch=3), moe.MOE_ERR_INVALID),
     (dict(single_launch=-1), moe.MOE_ERR_INVALID),
     (dict(batch=64, force_variant=moe.VARIANT_SMALL_M), moe.MOE_ERR_UNSUPPORTED),
@@ -120,17 +124,20 @@ def test_auto_variant(batch, variant):
     p = moe.Plan(cfg(batch=batch))
     info = p.info()
     assert info.variant == variant
-    # front (router + shared gate/up), [top-k], routed gate/up, down, [combine]:
-    # above batch 4 the router is an MFMA launch + a top-k launch, and the down
-    # projection is expert-major with a combine launch
+    # batch <= 4: router, gate/up (selecting for itself, shared gate/up
+    # included), down; above: router MFMA launch (+ shared gate/up), top-k
+    # launch, routed gate/up, expert-major down, combine
     big = 1 if batch > 4 else 0
     assert info.router_mfma == big
     assert info.single_launch == 0
     assert info.n_kernels == 3 + 2 * big
+    assert info.topk_launch == (2 if big else 3)
     assert info.layer_grid == 0
     assert info.shared_stream == 0
     assert info.workspace_bytes > 0
-    if variant == moe.VARIANT_SPLIT_K:
+    if not big:  # every gate/up tile is a GEMV tile in that form
+        assert info.mfma_min_tokens == 0 and info.shared_mfma == 0
+    elif variant == moe.VARIANT_SPLIT_K:
         assert info.mfma_min_tokens == 4
         assert info.shared_mfma == (1 if batch >= 4 else 0)
     else:
@@ -157,7 +164,7 @@ def test_auto_variant(batch, variant):
     (dict(inter=1536, shared_inter=1536, top_k=2), 1), (dict(inter=2560, shared_inter=0, top_k=1), 0),
     (dict(inter=2048, shared_inter=2048), 0),                  # h rows exceed the LDS budget
     (dict(hidden=16384, batch=4), 0),                          # activations exceed it
-    (dict(topk_launch=2), 0), (dict(shared_stream=1), 0),
+    (dict(topk_launch=2), 0), (dict(topk_launch=3), 0), (dict(shared_stream=1), 0),
 ])
 def test_single_launch_policy(kw, fused):
     p = moe.Plan(cfg(**kw))
@@ -170,6 +177,31 @@ def test_single_launch_policy(kw, fused):
     p = moe.Plan(cfg(single_launch=moe.SINGLE_OFF, **kw))
     assert p.info().single_launch == 0
     p.destroy()
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 4])
+def test_topk_launch_policy(batch):
+    def info(**kw):
+        p = moe.Plan(cfg(batch=batch, **kw))
+        i = p.info()
+        p.destroy()
+        return i
+    i = info()
+    assert i.topk_launch == 3 and i.n_kernels == 3 and i.mfma_min_tokens == 0 and i.shared_mfma == 0
+    i = info(topk_launch=3, shared_stream=1)
+    assert i.topk_launch == 3 and i.n_kernels == 4
+    i = info(topk_launch=1)
+    assert i.topk_launch == 1 and i.n_kernels == 3
+    i = info(topk_launch=2)
+    assert i.topk_launch == 2 and i.n_kernels == 4
+    # a caller's MFMA threshold the batch can reach keeps the selection in the router
+    i = info(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=1)
+    assert i.topk_launch == 1 and i.mfma_min_tokens == 1 and i.shared_mfma == 1
+    # one it cannot reach does not
+    i = info(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=batch + 1)
+    assert i.topk_launch == 3 and i.shared_mfma == 0
+    i = info(single_launch=moe.SINGLE_REQUIRED)
+    assert i.topk_launch == 0 and i.n_kernels == 1
 
 
 def test_forced_variant_and_threshold():

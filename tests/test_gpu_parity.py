@@ -86,6 +86,28 @@ def test_tp8_uniform(tp8, batch):
     assert info.single_launch == 0
 
 
+@pytest.mark.parametrize("topk_launch", [1, 2, 3])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4])
+def test_tp8_topk_launch_forms(tp8, batch, topk_launch):
+    """Batch <= 4: selection in the router's last workgroup (1), in a launch
+    of its own (2), or in every routed gate/up workgroup (3, the default)."""
+    shape = shape_of(synthetic.TP8)
+    m, st, info = check(tp8, shape, batch, "tp8 B=%d topk_launch=%d" % (batch, topk_launch),
+                        offset=40 * topk_launch, topk_launch=topk_launch)
+    assert info.topk_launch == topk_launch
+    if topk_launch == 3:  # GEMV tiles only, counted by routed workgroup 0
+        assert st.mfma_tiles == 0 and st.gemv_tiles == st.n_unique * (shape.inter // 4)
+
+
+@pytest.mark.parametrize("topk_launch", [1, 3])
+@pytest.mark.parametrize("batch", [1, 2, 3])
+def test_tiny_topk_launch_forms(tiny, batch, topk_launch):
+    shape = shape_of(synthetic.TINY)
+    m, st, info = check(tiny, shape, batch, "tiny B=%d topk_launch=%d" % (batch, topk_launch),
+                        topk_launch=topk_launch)
+    assert info.topk_launch == topk_launch
+
+
 @pytest.mark.parametrize("batch", [1, 2, 3, 4])
 def test_tp8_single_launch(tp8, batch):
     shape = shape_of(synthetic.TP8)
@@ -189,21 +211,26 @@ def test_tp8_zipf_skew(tp8_zipf):
     assert st.n_unique < 200
 
 
-@pytest.mark.parametrize("B,single", [(4, 0), (4, 2), (16, 0)])
-def test_tp8_identical_tokens_route_together(tp8, B, single):
-    """Every token identical: the k selected experts each get all B tokens, so
-    the routed experts go through the split-K MFMA tiles (inside the single
-    launch at B = 4)."""
+@pytest.mark.parametrize("B,single,topk_launch", [(4, 0, 0), (4, 0, 1), (4, 2, 0), (16, 0, 0)])
+def test_tp8_identical_tokens_route_together(tp8, B, single, topk_launch):
+    """Every token identical: the k selected experts each get all B tokens.
+    At B = 4 the default staged form runs them on GEMV tiles of 4 tokens; with
+    the selection in the router (topk_launch 1), inside the single launch and
+    at B = 16 they go through the split-K MFMA tiles."""
     shape = shape_of(synthetic.TP8)
     x1, _ = gap_x(tp8, shape, 1, offset=500)
     x = np.repeat(x1, B, axis=0)
-    plan = make_plan(tp8, shape, B, single_launch=single)
+    plan = make_plan(tp8, shape, B, single_launch=single, topk_launch=topk_launch)
     out, idx, w, nu = run_gpu(plan, tp8, x, shape)
     out64, idx_o, w_o = run_oracle(tp8, shape, x)
     compare(out, idx, w, out64, idx_o, w_o, "identical tokens")
     assert plan.info().single_launch == (1 if single else 0)
     st = plan.stats()
-    assert nu == 8 and st.mfma_tiles > 0 and st.gemv_tiles == 0
+    assert nu == 8
+    if B <= 4 and not single and topk_launch == 0:
+        assert st.mfma_tiles == 0 and st.gemv_tiles == 8 * (shape.inter // 4)
+    else:
+        assert st.mfma_tiles > 0 and st.gemv_tiles == 0
     plan.destroy()
 
 
@@ -261,9 +288,12 @@ def test_forwards_captured_into_a_caller_graph(tp8, batch, shared_stream):
     plan.destroy()
 
 
-def test_profiling_path_matches(tp8):
+@pytest.mark.parametrize("B,slots", [
+    (16, {"front", "topk_bucket", "gateup_routed", "down_combine", "combine"}),
+    (1, {"front", "gateup_routed", "down_combine"}),
+])
+def test_profiling_path_matches(tp8, B, slots):
     shape = shape_of(synthetic.TP8)
-    B = 16
     x, _ = gap_x(tp8, shape, B, offset=300)
     plan = make_plan(tp8, shape, B)
     plan.set_profiling(True)
@@ -271,7 +301,7 @@ def test_profiling_path_matches(tp8):
         out, idx, w, nu = run_gpu(plan, tp8, x, shape)
     prof = plan.profile_read()
     used = {k for k, v in prof.items() if v[1]}
-    assert used == {"front", "topk_bucket", "gateup_routed", "down_combine", "combine"}, prof
+    assert used == slots, prof
     assert all(prof[k][1] == 3 and prof[k][0] > 0 for k in used)
     out64, idx_o, w_o = run_oracle(tp8, shape, x)
     compare(out, idx, w, out64, idx_o, w_o, "profiled")
