@@ -213,6 +213,11 @@ KernelPick pick_down_x(const DownXArgs& a);
 KernelPick pick_combine(const DownXArgs& a);
 // Output-stationary down (down_rows over all entries) for small batches.
 KernelPick pick_down(const DownArgs& a);
+// Output-stationary down for batch <= 4 on v_dot2 with h in LDS as bf16 hi/lo
+// pairs; func is null where it does not apply (then pick_down).
+constexpr int kDownOsLds = 60 * 1024;
+KernelPick pick_down_os(const DownArgs& a);
+size_t down_os_lds_bytes(int B, int k, int I, int Is);
 // Single-launch layer; func is null when the shape has no instantiation.
 KernelPick pick_layer(const LayerArgs& L, size_t lds_bytes);
 int down_rows_per_block(int I);

@@ -386,7 +386,8 @@ void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, con
         p->kd = pick_down_x(p->dx);
         p->kc = pick_combine(p->dx);
     } else {
-        p->kd = pick_down(p->da);
+        p->kd = pick_down_os(p->da);
+        if (!p->kd.func) p->kd = pick_down(p->da);
     }
     if (p->fused) {
         p->la.f = p->fa;

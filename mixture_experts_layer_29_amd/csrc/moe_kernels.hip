@@ -300,6 +300,195 @@ __global__ __launch_bounds__(256) void down_combine_kernel(DownArgs a) {
     down_rows<LPR, NQ, RP, HLDS, DOWN_ALL, false>(a, blockIdx.x, s_h, s_acc, [] {});
 }
 
+// Packs 4 floats into bf16 hi and lo parts (v ~= hi + lo to ~2^-16 relative)
+// and stores them as pairs 2i, 2i+1 of s_hh and s_hl.
+__device__ __forceinline__ void store_hilo4(uint32_t* s_hh, uint32_t* s_hl, int i, float4 v) {
+    const uint32_t h0 = f32_to_bf16_rne(v.x), h1 = f32_to_bf16_rne(v.y);
+    const uint32_t h2 = f32_to_bf16_rne(v.z), h3 = f32_to_bf16_rne(v.w);
+    const uint32_t l0 = f32_to_bf16_rne(v.x - __uint_as_float(h0 << 16));
+    const uint32_t l1 = f32_to_bf16_rne(v.y - __uint_as_float(h1 << 16));
+    const uint32_t l2 = f32_to_bf16_rne(v.z - __uint_as_float(h2 << 16));
+    const uint32_t l3 = f32_to_bf16_rne(v.w - __uint_as_float(h3 << 16));
+    reinterpret_cast<uint2*>(s_hh)[i] = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
+    reinterpret_cast<uint2*>(s_hl)[i] = uint2{l0 | (l1 << 16), l2 | (l3 << 16)};
+}
+
+// Output-stationary down for batch <= TB <= 4 (staged launches).  Workgroup:
+// output rows [row0, row0 + R), R = 4 * 64 / LPR; wave w owns 64 / LPR of
+// them, LPR lanes per row (LPR <= 16), NQ 16-byte units per lane, so
+// 8 * LPR * NQ = I.  Entries: the nact active routed experts, then the shared
+// expert's nsh column blocks; CE per chunk, two chunks in flight.
+// Order of requests, so that the weights wait for one round trip at most:
+//   the entry count and the first 2*CE expert ids together (scalar; ids past
+//   the count are read but unused -- act_e is a 256-byte block);
+//   every slot's and token's h row, the slots' pair ids, the pairs' routing
+//   weights and the entries' slot offsets (vector, to LDS);
+//   the weights of the first two chunks once the scalars are in.
+// h goes to LDS as bf16 hi/lo pairs while the weights stream.  Per entry and
+// token: v_dot2 of W2 with h's hi and lo parts over the lane's units, an
+// LPR-lane DPP sum (every lane of the group ends with it), times the routing
+// weight into a register accumulator per token; entries then tokens in a
+// fixed order, so the sum is deterministic.
+template <int TB, int LPR, int NQ>
+__global__ __launch_bounds__(256) void down_os_kernel(DownArgs a) {
+    extern __shared__ __align__(16) uint32_t s_hp[];  // hi pairs [nrow][I/2], then lo pairs
+    constexpr int NP = TB * kMaxTopK;
+    __shared__ int32_t s_tok[NP];   // slot -> token
+    __shared__ float s_wsl[NP];     // slot -> routing weight
+    __shared__ int32_t s_perm[NP];  // staging: slot -> pair
+    __shared__ float s_tw[NP];      // staging: pair -> routing weight
+    __shared__ int32_t s_off[NP + 1];
+    __shared__ int32_t s_acte[NP];
+    static_assert(LPR <= 16, "every lane of a group needs the group sum");
+    constexpr int RW = 64 / LPR, R = 4 * RW;
+    constexpr int CE = (16 / NQ) > 0 ? 16 / NQ : 1;  // entries per chunk
+    static_assert(2 * CE <= 64, "the early ids stay inside act_e's 256-byte block");
+    constexpr int HREG = 3 * TB;                     // h float4 per thread requested before the weights
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H, I = a.I, B = a.B, k = a.k;
+    const int nsh = a.s2 ? a.Is / I : 0;
+    const int np = B * k, maxa = min(a.n_experts, np);
+    const int row = blockIdx.x * R + wave * RW + lane / LPR;
+    const int c = lane % LPR;
+    const size_t estride = (size_t)H * I;
+
+    const int nact = min(uni(*a.n_act), maxa);
+    int eid0[2 * CE];
+#pragma unroll
+    for (int i = 0; i < 2 * CE; ++i) eid0[i] = uni(a.act_e[i]);
+
+    // vector loads that need no work list: h rows (routed slots [0, np), then
+    // shared rows [np, np + B*nsh): hs is [B][nsh][I]), pair ids, weights, offsets
+    const int I4 = I / 4, nh4 = np * I4, nrow = np + B * nsh, n4 = nrow * I4;
+    float4 hv[HREG];
+#pragma unroll
+    for (int j = 0; j < HREG; ++j) {
+        const int i = tid + 256 * j;
+        const float* src = i < nh4 ? a.h + 4 * (size_t)i : a.hs + 4 * (size_t)(i < n4 ? i - nh4 : 0);
+        hv[j] = *reinterpret_cast<const float4*>(src);
+    }
+    int32_t pv = 0, ov = 0, ev = 0;
+    float twv = 0.0f;
+    if (tid < np) {
+        pv = a.perm[tid];
+        twv = a.topk_w[tid];
+    }
+    if (tid <= maxa) ov = a.act_off[tid];
+    if (tid < maxa) ev = a.act_e[tid];
+
+    const int total = nact + nsh;
+    // this lane's first unit of entry ent's row; e: the expert id when routed
+    auto w_of = [&](int ent, int e) -> const uint16_t* {
+        if (ent >= nact) return a.s2 + (size_t)row * a.Is + (size_t)(ent - nact) * I + 8 * c;
+        if ((unsigned)e >= (unsigned)a.n_experts) e = 0;  // bucketing never publishes this
+        return a.w2 + (size_t)e * estride + (size_t)row * I + 8 * c;
+    };
+    auto load_early = [&](int c0, u32x4 (&buf)[CE][NQ]) {  // c0 = 0 or CE
+#pragma unroll
+        for (int ce = 0; ce < CE; ++ce) {
+            const int ent = c0 + ce;
+            if (ent < total) {
+                const uint16_t* w = w_of(ent, eid0[c0 + ce]);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) buf[ce][q] = ld16(w + 8 * LPR * q);
+            }
+        }
+    };
+    auto load_later = [&](int c0, u32x4 (&buf)[CE][NQ]) {
+#pragma unroll
+        for (int ce = 0; ce < CE; ++ce) {
+            const int ent = c0 + ce;
+            if (ent < total) {
+                const uint16_t* w = w_of(ent, ent < nact ? uni(s_acte[ent]) : 0);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) buf[ce][q] = ld16(w + 8 * LPR * q);
+            }
+        }
+    };
+    u32x4 wb0[CE][NQ], wb1[CE][NQ];
+    load_early(0, wb0);
+    if (CE < total) load_early(CE, wb1);
+
+    uint32_t* s_hh = s_hp;
+    uint32_t* s_hl = s_hp + (size_t)nrow * I / 2;
+#pragma unroll
+    for (int j = 0; j < HREG; ++j) {
+        const int i = tid + 256 * j;
+        if (i < n4) store_hilo4(s_hh, s_hl, i, hv[j]);
+    }
+    for (int i = tid + 256 * HREG; i < n4; i += 256) {
+        const float* src = i < nh4 ? a.h + 4 * (size_t)i : a.hs + 4 * (size_t)(i - nh4);
+        store_hilo4(s_hh, s_hl, i, *reinterpret_cast<const float4*>(src));
+    }
+    if (tid < np) {
+        s_perm[tid] = pv;
+        s_tw[tid] = twv;
+    }
+    if (tid <= maxa) s_off[tid] = ov;
+    if (tid < maxa) s_acte[tid] = ev;
+    __syncthreads();
+    if (tid < np) {
+        const int p = s_perm[tid];
+        const bool ok = p >= 0 && p < np;  // bucketing never publishes a bad pair id
+        s_tok[tid] = ok ? p / k : 0;
+        s_wsl[tid] = ok ? s_tw[p] : 0.0f;
+    }
+    __syncthreads();
+
+    float acc[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
+    auto dot_row = [&](const u32x4 (&w)[NQ], int hrow) {
+        float d = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const size_t pe = (size_t)hrow * (I / 2) + 4 * (c + LPR * q);
+            d = dot8_hilo(w[q], *reinterpret_cast<const u32x4*>(s_hh + pe),
+                          *reinterpret_cast<const u32x4*>(s_hl + pe), d);
+        }
+        return group_sum<LPR>(d);
+    };
+    auto add = [&](int t, float v) {
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt)
+            if (tt == t) acc[tt] += v;
+    };
+    auto process = [&](int c0, const u32x4 (&wa)[CE][NQ]) {
+#pragma unroll
+        for (int ce = 0; ce < CE; ++ce) {
+            const int ent = c0 + ce;
+            if (ent < nact) {
+                if constexpr (TB == 1) {  // one token: entry ent is slot ent
+                    acc[0] += s_wsl[ent] * dot_row(wa[ce], ent);
+                } else {
+                    const int off = max(uni(s_off[ent]), 0), end = min(uni(s_off[ent + 1]), np);
+                    for (int sl = off; sl < end; ++sl) add(uni(s_tok[sl]), s_wsl[sl] * dot_row(wa[ce], sl));
+                }
+            } else if (ent < total) {
+                const int v = ent - nact;
+                for (int t = 0; t < B; ++t) add(t, dot_row(wa[ce], np + t * nsh + v));
+            }
+        }
+    };
+    for (int c0 = 0; c0 < total; c0 += 2 * CE) {
+        process(c0, wb0);
+        if (c0 + 2 * CE < total) load_later(c0 + 2 * CE, wb0);
+        if (c0 + CE >= total) break;
+        process(c0 + CE, wb1);
+        if (c0 + 3 * CE < total) load_later(c0 + 3 * CE, wb1);
+    }
+    if (c == 0) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            if (t < B) {
+                float v = acc[t];
+                if (a.add_residual) v += __uint_as_float((uint32_t)a.x[(size_t)t * H + row] << 16);
+                a.out[(size_t)t * H + row] = f32_to_bf16_rne(v);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // down, expert-major (staged launches, larger batches)
 // ---------------------------------------------------------------------------
@@ -715,6 +904,32 @@ KernelPick pick_down(const DownArgs& a) {
     const size_t lds = hl ? down_h_lds_bytes(a.B, a.k, a.I, a.s2 ? a.Is : 0) : (size_t)kDownHStage;
     return {f, dim3(a.H / down_rows_per_block(a.I)), dim3(256), lds};
 }
+
+// Output-stationary down for batch <= 4, or a null func when the shape has no
+// instantiation (I in {64, 128, 256, 512, 1024}) or h exceeds kDownOsLds.
+KernelPick pick_down_os(const DownArgs& a) {
+    const int ur = a.I / 8, tb = tb_bucket(a.B);
+    const size_t lds = down_os_lds_bytes(a.B, a.k, a.I, a.s2 ? a.Is : 0);
+    const void* f = nullptr;
+    int lpr = 16;
+    if (a.B <= 4 && lds <= (size_t)kDownOsLds) {
+#define MOE_DO(LPR, NQ) \
+    f = tb == 1 ? MOE_FN((down_os_kernel<1, LPR, NQ>)) : tb == 2 ? MOE_FN((down_os_kernel<2, LPR, NQ>)) \
+                                                           : MOE_FN((down_os_kernel<4, LPR, NQ>));
+        switch (ur) {
+            case 8: MOE_DO(8, 1) lpr = 8; break;
+            case 16: MOE_DO(16, 1) break;
+            case 32: MOE_DO(16, 2) break;
+            case 64: MOE_DO(16, 4) break;
+            case 128: MOE_DO(16, 8) break;
+            default: break;
+        }
+#undef MOE_DO
+    }
+    return {f, dim3(a.H / (4 * 64 / lpr)), dim3(256), lds};
+}
+
+size_t down_os_lds_bytes(int B, int k, int I, int Is) { return ((size_t)B * k + (size_t)B * (Is / I)) * I * 4; }
 
 KernelPick pick_combine(const DownXArgs& a) {
     return {MOE_FN(combine_kernel), dim3((a.B * a.H / 4 + 255) / 256), dim3(256), 0};
