@@ -148,15 +148,18 @@ struct FrontArgs {
 };
 
 // Gate/up launch that selects for itself (batch <= 4; the front launch before
-// it writes the logits z with the bias added and the shared expert's h):
-// every workgroup reads z, selects the top-k of all B tokens (one wave per
-// token) and buckets the pairs in LDS, then runs the tile of the active
-// expert its index maps to.  Workgroup 0 also writes the routing rows and the
+// it writes the logits z with the bias added): every workgroup reads z,
+// selects the top-k of all B tokens (one wave per token) and buckets the
+// pairs in LDS, then runs the tile of the active expert its index maps to;
+// workgroups [0, shared_pairs) first compute one of the shared expert's
+// gate/up row pairs, whose weights stream during the selection.  Workgroup 0 also writes the routing rows and the
 // work lists for the down launch and the caller.  Every workgroup computes the
 // same lists, so there is no hand-off inside the launch.
 struct SelGateUpArgs {
     RouterArgs r;           // logits (r.z) and the routing / work-list outputs
     GateUpArgs g;           // routed experts
+    GateUpArgs s;           // shared expert (row pairs [0, shared_pairs), one per workgroup)
+    int32_t shared_pairs;   // 0: the shared gate/up runs elsewhere
 };
 
 // Whole layer in one launch (batch <= 4): tasks in dependency order

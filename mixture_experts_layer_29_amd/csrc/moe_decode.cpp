@@ -289,9 +289,15 @@ void fill_static_args(moe_decode_plan_s* p) {
         s.kslice = p->kslice;
     }
 
-    // the select-in-gate/up form's front: one router row / shared row pair per workgroup
+    // The select-in-gate/up form: the front computes one router row per
+    // workgroup; the shared expert's gate/up row pairs run in the gate/up
+    // launch (one per workgroup, during the selection) when it has enough
+    // workgroups, else in the front, one pair per workgroup.
     p->fa.router_blocks = p->select_in_gateup ? c.n_experts : front_router_blocks(r, p->small_router);
-    p->fa.shared_blocks = !shared_in_front(p) ? 0
+    const bool sh_sel = p->select_in_gateup && shared_in_front(p) &&
+                        c.shared_inter <= p->max_act * (c.inter / kPairsPerGemvTile);
+    p->sga.shared_pairs = sh_sel ? c.shared_inter : 0;
+    p->fa.shared_blocks = !shared_in_front(p) || sh_sel ? 0
                           : p->select_in_gateup ? c.shared_inter : c.shared_inter / kPairsPerGemvTile;
 
     DownArgs& d = p->da;
@@ -374,6 +380,7 @@ void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, con
     if (p->select_in_gateup) {
         p->sga.r = p->ra;
         p->sga.g = p->ga;
+        p->sga.s = p->gs;
         p->kf = pick_front_split(p->fa);
         p->kg = pick_gateup_select(p->sga, p->max_act);
     } else {

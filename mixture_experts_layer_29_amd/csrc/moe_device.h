@@ -491,16 +491,22 @@ __device__ __forceinline__ void bucket_block(const RouterArgs& a, const int32_t*
 // holds the selected ids of the workgroup's tokens.  !to_global: the routing
 // rows (topk_idx / topk_w) are not written.  COH: src was written by other
 // workgroups of this launch (coherent loads); else by an earlier launch.
-template <int NS, bool COH = true>
+// mid() runs in every wave once the logit loads are issued and before they
+// are used: loads it issues complete after them.
+struct NoMid {
+    __device__ void operator()() const {}
+};
+template <int NS, bool COH = true, class Mid = NoMid>
 __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float* src, const float* bias,
-                                              bool from_acc, int32_t* s_pair_e, bool to_global = true) {
+                                              bool from_acc, int32_t* s_pair_e, bool to_global = true,
+                                              Mid&& mid = Mid{}) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = a.E, B = a.B, k = a.k;
     const int t = t0 + wave;
+    float* row = src + (size_t)t * E;
+    float* zo = a.z + (size_t)t * E;
+    float v[NS];
     if (t < B) {
-        float* row = src + (size_t)t * E;
-        float* zo = a.z + (size_t)t * E;
-        float v[NS];
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
             const int e = m * 64 + lane;
@@ -516,12 +522,15 @@ __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float
             }
             v[m] = x;
         }
+    }
+    mid();
+    if (t < B) {
         int my_e;
         float my_z;
         topk_wave<NS>(v, E, k, lane, my_e, my_z);
         // a full softmax reads the token's logits back: from_acc rows are in a.z (this
         // wave's stores, complete after the wait)
-        __builtin_amdgcn_s_waitcnt(0);
+        if (from_acc) __builtin_amdgcn_s_waitcnt(0);
         route_one(a, t, lane, from_acc ? zo : row, my_e, my_z, __shfl(my_z, 0, 64), s_pair_e, to_global);
     }
     __syncthreads();

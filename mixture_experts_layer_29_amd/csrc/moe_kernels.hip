@@ -233,6 +233,9 @@ __global__ __launch_bounds__(256) void front_split_kernel(FrontArgs f) {
 // workgroup runs tile `local` of entry `entry` with the entry's token ids from
 // LDS.  Every workgroup derives the same lists from the same logits.  At
 // B = 1 the k experts are distinct, so pair j is entry j in slot j.
+// Workgroups b < shared_pairs also compute the shared expert's gate/up row
+// pair b: its loads go out right behind the logit loads, so they stream while
+// the selection runs (the weights of the routed tile are not known yet).
 template <int TB, int NS>
 __global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
     extern __shared__ __align__(16) uint16_t s_x[];  // [B][H]
@@ -241,12 +244,33 @@ __global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
     __shared__ int32_t s_act_e[4 * kMaxTopK];
     __shared__ int32_t s_act_off[4 * kMaxTopK + 1];
     __shared__ int32_t s_nact;
+    __shared__ float s_part[4][2][TB];
     const RouterArgs& a = sa.r;
     const GateUpArgs& g = sa.g;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const GateUpArgs& sg = sa.s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x;
     const bool out = b == 0;
-    select_tokens<NS, false>(a, 0, a.z, nullptr, false, s_pair_e, out);
+    // shared row pair b: the first 1024 units of K requested during the selection
+    constexpr int Q = 4;
+    const bool shp = b < sa.shared_pairs;
+    const int units = sg.H >> 3;
+    const u32x4 zero = u32x4{0, 0, 0, 0};
+    const uint16_t* srow[2] = {sg.w + (size_t)b * sg.H, sg.w + (size_t)(sg.n + b) * sg.H};
+    u32x4 swv[Q][2], sxv[Q][TB];
+    auto issue_shared = [&]() {
+        if (!shp) return;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int u = 256 * q + tid;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) swv[q][r] = u < units ? ld16(srow[r] + u * 8) : zero;
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                sxv[q][t] = (u < units && t < a.B) ? ld16(sg.x + (size_t)t * sg.H + u * 8) : zero;
+        }
+    };
+    select_tokens<NS, false>(a, 0, a.z, nullptr, false, s_pair_e, out, issue_shared);
     if (tid < 64) {
         const int np = a.B * a.k;
         const int e = lane < np ? s_pair_e[lane] : kNone;
@@ -276,6 +300,50 @@ __global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
         }
     }
     __syncthreads();
+    if (shp) {  // finish the shared row pair: the rest of K, then the wave sums in a fixed order
+        float acc[2][TB];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int t = 0; t < TB; ++t) acc[r][t] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int t = 0; t < TB; ++t)
+                    if (t < a.B) acc[r][t] = dot8(swv[q][r], sxv[q][t], acc[r][t]);
+        for (int u = 256 * Q + tid; u < units; u += 256)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const u32x4 w = ld16(srow[r] + u * 8);
+#pragma unroll
+                for (int t = 0; t < TB; ++t)
+                    if (t < a.B) acc[r][t] = dot8(w, ld16(sg.x + (size_t)t * sg.H + u * 8), acc[r][t]);
+            }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                if (t < a.B) {
+                    const float sum = wave_sum(acc[r][t]);
+                    if (lane == 0) s_part[wave][r][t] = sum;
+                }
+            }
+        __syncthreads();
+        if (tid < a.B) {
+            float gu[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                float v = 0.0f;
+#pragma unroll
+                for (int t = 0; t < TB; ++t)
+                    if (t == tid) v = (s_part[0][r][t] + s_part[1][r][t]) + (s_part[2][r][t] + s_part[3][r][t]);
+                gu[r] = v;
+            }
+            sg.h[(size_t)tid * sg.n + b] = silu_f(gu[0]) * gu[1];
+        }
+    }
     const int entry = b / g.tiles_per_expert, local = b % g.tiles_per_expert;
     if (entry >= uni(s_nact)) return;
     const int e = uni(s_act_e[entry]), off = uni(s_act_off[entry]);
