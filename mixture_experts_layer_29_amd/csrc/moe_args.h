@@ -48,8 +48,9 @@ struct RouterArgs {
     const uint16_t* wr;     // bf16 [E][H]
     const float* bias;      // fp32 [E] or null
     float* z;               // fp32 [B][E] logits (workspace)
-    float* zacc;            // fp32 [B][E] split-K partial logits (zero between uses)
-    int32_t ksplit, kslice; // MFMA router: K splits and K elements per split
+    float* zacc;            // fp32 [nzpart][B][E] partial logits for a later top-k launch
+    int32_t nzpart;         // partial slices in zacc (1: full sums)
+    int32_t ksplit, kslice; // MFMA gate/up tiles: K splits and K elements per split
     int32_t* topk_idx;      // [B][k]
     float* topk_w;          // [B][k]
     int32_t* meta;
@@ -145,6 +146,22 @@ struct FrontArgs {
     GateUpArgs s;           // shared expert work list (ignored when shared_blocks == 0)
     int32_t router_blocks;  // workgroups [0, router_blocks) run the router
     int32_t shared_blocks;  // workgroups [router_blocks, +shared_blocks) run the shared gate/up
+    // dense split-K form (batch > 4): tiles of 16 rows x one of `dks` K splits
+    // of `dsteps` 32-wide steps; router partials to r.zacc, shared gate/up
+    // partials [dks][B][2 Is] to `spart`
+    float* spart;
+    int32_t dks, dsteps;
+};
+
+// Top-k launch (batch > 4): workgroups [0, sel_blocks) select and bucket
+// (four tokens each); the rest reduce the shared expert's gate/up partials
+// to h_s = silu(sum gate) * sum up, one (token, row) per thread.
+struct TopkArgs {
+    RouterArgs r;
+    const float* spart;     // fp32 [nspart][B][2 Is] or null
+    float* hs;              // fp32 [B][Is]
+    int32_t Is, nspart;
+    int32_t sel_blocks;
 };
 
 // Gate/up launch that selects for itself (batch <= 4; the front launch before
@@ -202,7 +219,9 @@ KernelPick pick_init(const InitArgs& a);
 // expert uses MFMA tiles, else its GEMV token count.
 KernelPick pick_front(const FrontArgs& f, bool small_router, bool select_in_router, int shared_tb);
 int front_router_blocks(const RouterArgs& a, bool small_router);
-KernelPick pick_topk(const RouterArgs& a);
+KernelPick pick_topk(const TopkArgs& a);
+// Dense split-K front (router + shared gate/up partials) for batch > 4.
+KernelPick pick_front_dense(const FrontArgs& f);
 // Front launch of the select-in-gate/up form (batch <= 4): f.router_blocks
 // (= E) router rows, then f.shared_blocks (= Is or 0) shared gate/up row
 // pairs, one per workgroup, K split over its four waves.

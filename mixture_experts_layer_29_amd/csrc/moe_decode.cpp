@@ -71,7 +71,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
     size_t meta, z, zacc, topk_idx, topk_w, act_e, act_off, perm, sh_act_e, sh_act_off, sh_perm;
-    size_t h, hs, g_acc, g_acc_s, tile_cnt, tile_cnt_s, s_out, part, part_s, total;
+    size_t h, hs, g_acc, g_acc_s, tile_cnt, tile_cnt_s, s_out, part, part_s, spart, total;
 };
 
 }  // namespace
@@ -84,6 +84,7 @@ struct moe_decode_plan_s {
     bool shared_mfma;
     int max_act;          // min(E, B*k)
     int ksplit, kslice;
+    int dks, dsteps;      // dense front (batch > 4): K splits and 32-wide steps per split
     bool small_router;    // batch <= 4: one router launch; else MFMA router + top-k launch
     bool shared_stream;   // shared gate/up on the second stream instead of the front launch
     bool select_in_router;// batch <= 4: top-k + bucketing in the router's last workgroup
@@ -106,6 +107,7 @@ struct moe_decode_plan_s {
     RouterArgs& ra = fa.r;
     GateUpArgs& gs = fa.s;
     GateUpArgs ga{};
+    TopkArgs ta{};        // top-k launch (router part refreshed per forward)
     SelGateUpArgs sga{};  // gate/up launch of the select-in-gate/up form
     DownArgs da{};     // down of the single launch
     DownXArgs dx{};    // down of the staged launches
@@ -178,7 +180,8 @@ moe_status validate(const moe_decode_config* c) {
     return MOE_OK;
 }
 
-Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fused, bool expert_major) {
+Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fused, bool expert_major, int nzpart,
+                   int nspart) {
     const size_t B = c.batch, E = c.n_experts, k = c.top_k, I = c.inter, Is = c.shared_inter;
     Layout L{};
     size_t o = 0;
@@ -189,7 +192,7 @@ Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fus
     };
     L.meta = take(M_COUNT * 4);
     L.z = take(B * E * 4);
-    L.zacc = take(B * E * 4);
+    L.zacc = take((size_t)nzpart * B * E * 4);
     L.topk_idx = take(B * k * 4);
     L.topk_w = take(B * k * 4);
     L.act_e = take((size_t)max_act * 4);
@@ -211,6 +214,7 @@ Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fus
         L.part = take(B * k * c.hidden * 4);
         L.part_s = take((Is / I) * B * c.hidden * 4 + 4);
     }
+    if (nspart) L.spart = take((size_t)nspart * B * 2 * Is * 4);
     L.total = o;
     return L;
 }
@@ -228,6 +232,7 @@ void fill_static_args(moe_decode_plan_s* p) {
     r.bias = c.router_bias;
     r.z = at<float>(p, p->L.z);
     r.zacc = at<float>(p, p->L.zacc);
+    r.nzpart = p->small_router ? 1 : p->dks;
     r.ksplit = p->ksplit;
     r.kslice = p->kslice;
     r.topk_idx = at<int32_t>(p, p->L.topk_idx);
@@ -293,12 +298,24 @@ void fill_static_args(moe_decode_plan_s* p) {
     // workgroup; the shared expert's gate/up row pairs run in the gate/up
     // launch (one per workgroup, during the selection) when it has enough
     // workgroups, else in the front, one pair per workgroup.
-    p->fa.router_blocks = p->select_in_gateup ? c.n_experts : front_router_blocks(r, p->small_router);
+    p->fa.router_blocks = p->select_in_gateup ? c.n_experts
+                          : p->small_router     ? front_router_blocks(r, true)
+                                                : ((c.n_experts + 15) / 16) * p->dks;
     const bool sh_sel = p->select_in_gateup && shared_in_front(p) &&
                         c.shared_inter <= p->max_act * (c.inter / kPairsPerGemvTile);
     p->sga.shared_pairs = sh_sel ? c.shared_inter : 0;
     p->fa.shared_blocks = !shared_in_front(p) || sh_sel ? 0
-                          : p->select_in_gateup ? c.shared_inter : c.shared_inter / kPairsPerGemvTile;
+                          : p->select_in_gateup ? c.shared_inter
+                          : p->small_router     ? c.shared_inter / kPairsPerGemvTile
+                                                : (2 * c.shared_inter / 16) * p->dks;
+    p->fa.dks = p->dks;
+    p->fa.dsteps = p->dsteps;
+    p->fa.spart = p->L.spart ? at<float>(p, p->L.spart) : nullptr;
+    p->ta.spart = p->fa.spart;
+    p->ta.hs = at<float>(p, p->L.hs);
+    p->ta.Is = c.shared_inter;
+    p->ta.nspart = p->L.spart ? p->dks : 0;
+    p->ta.sel_blocks = (c.batch + 3) / 4;
 
     DownArgs& d = p->da;
     d.n_act = g.n_act;
@@ -385,7 +402,10 @@ void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, con
         p->kg = pick_gateup_select(p->sga, p->max_act);
     } else {
         p->kf = pick_front(p->fa, p->small_router, p->select_in_router, p->shared_mfma ? 0 : c.batch);
-        if (topk_own_launch(p)) p->kt = pick_topk(p->ra);
+        if (topk_own_launch(p)) {
+            p->ta.r = p->ra;
+            p->kt = pick_topk(p->ta);
+        }
         p->kg = pick_gateup(p->ga, p->max_act, p->routed_gemv_tb);
     }
     if (has_shared(p) && p->shared_stream) p->ks = pick_gateup(p->gs, 1, p->shared_mfma ? 1 : c.batch);
@@ -482,7 +502,7 @@ moe_status enqueue_eager(moe_decode_plan_s* p, hipStream_t stream, hipEvent_t* e
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT + 1], stream));
     if (topk_own_launch(p)) {
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_TOPK], stream));
-        if ((st = launch(p->kt, &p->ra, stream))) return st;
+        if ((st = launch(p->kt, &p->ta, stream))) return st;
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_TOPK + 1], stream));
     }
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_GATEUP], stream));
@@ -521,7 +541,7 @@ moe_status build_graph(moe_decode_plan_s* p) {
         return MOE_OK;
     }
     void* af[] = {&p->fa};
-    void* ar[] = {&p->ra};
+    void* ar[] = {&p->ta};
     void* ag[] = {gateup_args(p)};
     void* as[] = {&p->gs};
     void* ad[] = {p->expert_major ? (void*)&p->dx : (void*)&p->da};
@@ -561,7 +581,7 @@ moe_status patch_graph(moe_decode_plan_s* p) {
         return MOE_OK;
     }
     void* af[] = {&p->fa};
-    void* ar[] = {&p->ra};
+    void* ar[] = {&p->ta};
     void* ag[] = {gateup_args(p)};
     void* as[] = {&p->gs};
     void* ad[] = {p->expert_major ? (void*)&p->dx : (void*)&p->da};
@@ -639,6 +659,19 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
     for (int s = kSplitK; s >= 1; --s)
         if (c.hidden % (32 * s) == 0) { p->ksplit = s; break; }
     p->kslice = c.hidden / p->ksplit;
+    // dense front: the fewest K splits (<= 32) that leave at most 16 steps of
+    // 32 per split (one round of loads per wave), else the most splits <= 32
+    {
+        const int steps = c.hidden / 32;
+        int d = 0;
+        for (int s = 1; s <= 32 && !d; ++s)
+            if (steps % s == 0 && steps / s <= 16) d = s;
+        if (!d)
+            for (int s = 32; s >= 1 && !d; --s)
+                if (steps % s == 0) d = s;
+        p->dks = d;
+        p->dsteps = steps / d;
+    }
     // single launch: batch <= 4, activations and every h row fit the LDS budget,
     // a down shape with an instantiation (I = 64, 128, 256 or 512..2048)
     {
@@ -686,7 +719,9 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
         return fail(MOE_ERR_UNSUPPORTED, "topk_launch = 3 needs batch <= 4 with x in the LDS budget");
     }
     p->expert_major = c.batch > kDownOsMaxBatch;
-    p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K, p->fused, p->expert_major);
+    p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K, p->fused, p->expert_major,
+                       p->small_router ? 1 : p->dks,
+                       !p->small_router && c.shared_inter > 0 && !p->shared_stream ? p->dks : 0);
     *out_plan = p;
     return MOE_OK;
 }

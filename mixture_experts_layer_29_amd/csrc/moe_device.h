@@ -485,9 +485,9 @@ __device__ __forceinline__ void bucket_block(const RouterArgs& a, const int32_t*
 }
 
 // Selection for tokens t0 + wave of this workgroup, one wave per token.
-// src: per-token logit rows (E floats); with `from_acc` they are split-K
-// accumulators: the bias is added, the sum stored to a.z and the accumulator
-// cleared.  Ends with a workgroup barrier, after which s_pair_e (if given)
+// src: per-token logit rows (E floats); with `from_acc` they are the first of
+// a.nzpart split-K partial slices [nzpart][B][E] written by an earlier launch:
+// they are summed, the bias is added and the logits stored to a.z.  Ends with a workgroup barrier, after which s_pair_e (if given)
 // holds the selected ids of the workgroup's tokens.  !to_global: the routing
 // rows (topk_idx / topk_w) are not written.  COH: src was written by other
 // workgroups of this launch (coherent loads); else by an earlier launch.
@@ -506,7 +506,40 @@ __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float
     float* row = src + (size_t)t * E;
     float* zo = a.z + (size_t)t * E;
     float v[NS];
-    if (t < B) {
+    if (t < B && from_acc) {
+        // partial logits [nzpart][B][E] written by the launch before, summed in
+        // a fixed order; QC partials per round, every load of a round issued
+        // before the first add (clamped addresses, masked adds)
+        constexpr int QC = NS <= 8 ? 8 : 4;
+        const int nz = a.nzpart;
+        const size_t qs = (size_t)B * E;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) v[m] = 0.0f;
+        for (int q0 = 0; q0 < nz; q0 += QC) {
+            float tmp[QC][NS];
+#pragma unroll
+            for (int qq = 0; qq < QC; ++qq) {
+                const size_t q = (size_t)min(q0 + qq, nz - 1);
+#pragma unroll
+                for (int m = 0; m < NS; ++m) tmp[qq][m] = row[q * qs + min(m * 64 + lane, E - 1)];
+            }
+#pragma unroll
+            for (int qq = 0; qq < QC; ++qq)
+#pragma unroll
+                for (int m = 0; m < NS; ++m)
+                    if (q0 + qq < nz) v[m] += tmp[qq][m];
+        }
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+            const int e = m * 64 + lane;
+            if (e < E) {
+                v[m] += bias ? bias[e] : 0.0f;
+                st_dev(zo + e, v[m]);
+            } else {
+                v[m] = -INFINITY;
+            }
+        }
+    } else if (t < B) {
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
             const int e = m * 64 + lane;
@@ -514,11 +547,6 @@ __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float
             if (e < E) {
                 if constexpr (COH) x = ld_dev(row + e);
                 else x = row[e];
-                if (from_acc) {
-                    x += bias ? bias[e] : 0.0f;
-                    st_dev(zo + e, x);
-                    st_dev(row + e, 0.0f);
-                }
             }
             v[m] = x;
         }
@@ -615,63 +643,74 @@ __device__ __forceinline__ void router_rows(const RouterArgs& a, int blk, uint16
 
 
 // ---------------------------------------------------------------------------
-// front launch, batch > 4: split-K MFMA router GEMM into zacc, plus the
-// shared expert's gate/up in trailing workgroups; then topk_bucket
+// front launch, batch > 4: dense split-K MFMA tiles (router logits and the
+// shared expert's gate/up rows) writing fp32 partials; topk_bucket sums them
 // ---------------------------------------------------------------------------
 
-// Tile: 64 router rows (16 per wave) x one K slice x all B tokens.
-// A = router rows (16 x 32), B = x^T (32 x 16 tokens), fp32 atomics into zacc.
-__device__ __forceinline__ void router_mfma_tile(const RouterArgs& a, int tile) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = a.H, E = a.E, B = a.B;
-    const int r0 = (tile / a.ksplit) * kRouterRowsPerMfmaTile + wave * 16;
+// One tile: 16 rows of W [nrows][H] x one K split of `ksteps` 32-wide steps x
+// all B <= 16*NT tokens.  The four waves take interleaved steps of the split
+// (wave w: steps w, w+4, ...), so a wave issues all its weight and activation
+// loads of a round of four steps before its first MFMA; the waves' 16 x B
+// accumulators are summed in LDS and stored as partial [ks][B][nrows] with
+// plain stores: no atomics, no counters, nothing to re-arm.  The consumer (the
+// next launch) sums the nks partials in a fixed order.
+// MFMA 16x16x32 bf16: A = 16 weight rows x 32 K (lane: row lane%16, K group
+// lane/16), B = x^T 32 K x 16 tokens (lane: token lane%16, K group lane/16);
+// D: lane holds rows 4*(lane/16)+r of token lane%16.
+template <int NT>
+__device__ __forceinline__ void dense_splitk_tile(const uint16_t* W, int nrows, const uint16_t* x, int B, int H,
+                                                  int ksteps, int rb, int ks, float* part, float* s_red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tl = lane & 15, kq = lane >> 4;
-    const int kbeg = (tile % a.ksplit) * a.kslice;
-    const int nsteps = min(a.kslice, H - kbeg) >> 5;
-    const int NT = (B + 15) >> 4;
-    const bool rok = r0 + tl < E;
-    const uint16_t* ar = a.wr + (size_t)(rok ? r0 + tl : 0) * H + kbeg + 8 * kq;
-    const uint16_t* xr[4];
-    bool xok[4];
+    const int r0 = rb * 16;
+    const bool rok = r0 + tl < nrows;
+    const uint16_t* wr = W + (size_t)(rok ? r0 + tl : 0) * H + (size_t)ks * ksteps * 32 + 8 * kq;
+    const uint16_t* xr[NT];
+    bool xok[NT];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < NT; ++tt) {
         const int t = tt * 16 + tl;
         xok[tt] = t < B;
-        xr[tt] = a.x + (size_t)(xok[tt] ? t : 0) * H + kbeg + 8 * kq;
+        xr[tt] = x + (size_t)(xok[tt] ? t : 0) * H + (size_t)ks * ksteps * 32 + 8 * kq;
     }
     const u32x4 zero = u32x4{0, 0, 0, 0};
-    f32x4 c[4];
+    f32x4 c[NT];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) c[tt] = f32x4{0, 0, 0, 0};
-    for (int s = 0; s < nsteps; s += 4) {
-        u32x4 A[4], X[4][4];
+    for (int tt = 0; tt < NT; ++tt) c[tt] = f32x4{0, 0, 0, 0};
+    for (int base = wave; base < ksteps; base += 16) {
+        u32x4 A[4], X[4][NT];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const bool sok = s + u < nsteps;
-            A[u] = (sok && rok) ? ld16(ar + 32 * (s + u)) : zero;
+            const int s = base + 4 * u;
+            const bool sok = s < ksteps;
+            A[u] = (sok && rok) ? ld16(wr + 32 * s) : zero;
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-                X[u][tt] = (sok && tt < NT && xok[tt]) ? ld16(xr[tt] + 32 * (s + u)) : zero;
+            for (int tt = 0; tt < NT; ++tt) X[u][tt] = (sok && xok[tt]) ? ld16(xr[tt] + 32 * s) : zero;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
+            if (base + 4 * u < ksteps)
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-                if (s + u < nsteps && tt < NT)
+                for (int tt = 0; tt < NT; ++tt)
                     c[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[u]),
-                                                                    __builtin_bit_cast(bf16x8, X[u][tt]),
-                                                                    c[tt], 0, 0, 0);
+                                                                    __builtin_bit_cast(bf16x8, X[u][tt]), c[tt],
+                                                                    0, 0, 0);
     }
-    // D layout: lane holds rows 4*(lane/16)+r, column (token) lane%16
+    // s_red[wave][tt][r][lane]
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int t = tt * 16 + tl;
-        if (tt < NT && t < B) {
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = r0 + 4 * kq + r;
-                if (row < E) atomicAdd(&a.zacc[(size_t)t * E + row], c[tt][r]);
-            }
+        for (int r = 0; r < 4; ++r) s_red[((wave * NT + tt) * 4 + r) * 64 + lane] = c[tt][r];
+    __syncthreads();
+    // thread -> (token t, row 0..15), 16 consecutive rows of one token per 16 threads
+    for (int idx = tid; idx < NT * 256; idx += 256) {
+        const int t = idx >> 4, row = idx & 15;
+        const int tt = t >> 4, src = (row >> 2) * 16 + (t & 15), r = row & 3;
+        if (t < B && r0 + row < nrows) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) v += s_red[((w * NT + tt) * 4 + r) * 64 + src];
+            part[((size_t)ks * B + t) * nrows + r0 + row] = v;
         }
     }
 }

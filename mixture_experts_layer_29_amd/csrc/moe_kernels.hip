@@ -62,36 +62,70 @@ __global__ __launch_bounds__(256) void front_small_kernel(FrontArgs f) {
     if ((threadIdx.x >> 6) == 0) bucket_wave(a, s_pair_e, threadIdx.x & 63);
 }
 
-template <int SHTB>  // 0: the shared expert runs on MFMA tiles, else its GEMV token bucket
-__global__ __launch_bounds__(256) void front_mfma_kernel(FrontArgs f) {
-    extern __shared__ __align__(16) uint16_t s_x[];
-    if ((int)blockIdx.x >= f.router_blocks) {
-        const int local = blockIdx.x - f.router_blocks;
-        if constexpr (SHTB == 0) mfma_gateup_tile<4>(f.s, f.s.w, 0, 0, f.r.B, local);
-        else gemv_gateup_tile<SHTB>(f.s, f.s.w, 0, f.r.B, local, s_x);
-        return;
+// Dense split-K front (batch > 4): router tiles, then the shared expert's
+// gate/up tiles (gate and up rows are independent rows here; the top-k launch
+// pairs them).  Every tile is one round of loads: many small tiles keep the
+// whole chip streaming the 12.8 MB of the TP8-shard shape at once.
+template <int NT>
+__global__ __launch_bounds__(256) void front_dense_kernel(FrontArgs f) {
+    __shared__ float s_red[4 * NT * 4 * 64];
+    const RouterArgs& a = f.r;
+    const int b = blockIdx.x;
+    if (b < f.router_blocks) {
+        dense_splitk_tile<NT>(a.wr, a.E, a.x, a.B, a.H, f.dsteps, b / f.dks, b % f.dks, a.zacc, s_red);
+    } else {
+        const int l = b - f.router_blocks;
+        dense_splitk_tile<NT>(f.s.w, 2 * f.s.n, a.x, a.B, a.H, f.dsteps, l / f.dks, l % f.dks, f.spart, s_red);
     }
-    router_mfma_tile(f.r, blockIdx.x);
 }
 
-// Logits = zacc + bias (zacc re-armed to zero), top-k, weights, bucketing.
-// With one workgroup (batch <= 4) everything stays in registers and LDS: no
-// atomics, fences or reloads sit between reading the logits and writing the
-// buckets.  With several, the last workgroup to arrive buckets all pairs.
+// Logits = sum of the partial slices + bias, top-k, weights, bucketing.
+// With one selecting workgroup (batch <= 4) everything stays in registers and
+// LDS: no atomics, fences or reloads sit between reading the logits and
+// writing the buckets.  With several, the last selecting workgroup to arrive
+// buckets all pairs.  Workgroups from sel_blocks on reduce the shared
+// expert's gate/up partials into h_s.
 template <int NS>
-__global__ __launch_bounds__(256) void topk_bucket_kernel(RouterArgs a) {
+__global__ __launch_bounds__(256) void topk_bucket_kernel(TopkArgs ta) {
     __shared__ int32_t s_pair_e[kMaxBatch * kMaxTopK];
     __shared__ int32_t s_rank[kMaxBatch * kMaxTopK];
     __shared__ int32_t s_cnt[kMaxExperts];
     __shared__ int32_t s_tmp[8];
     __shared__ int32_t s_nmfma;
     __shared__ int s_flag;
+    const RouterArgs& a = ta.r;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if ((int)blockIdx.x >= ta.sel_blocks) {
+        const int idx = (blockIdx.x - ta.sel_blocks) * 256 + tid;
+        const int Is = ta.Is, n2 = 2 * Is;
+        if (idx >= a.B * Is) return;
+        const int t = idx / Is, i = idx - t * Is;
+        const size_t qs = (size_t)a.B * n2;
+        const float* p = ta.spart + (size_t)t * n2 + i;
+        float g = 0.0f, u = 0.0f;
+        for (int q0 = 0; q0 < ta.nspart; q0 += 8) {
+            float tg[8], tu[8];
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq) {
+                const size_t q = (size_t)min(q0 + qq, ta.nspart - 1);
+                tg[qq] = p[q * qs];
+                tu[qq] = p[q * qs + Is];
+            }
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq)
+                if (q0 + qq < ta.nspart) {
+                    g += tg[qq];
+                    u += tu[qq];
+                }
+        }
+        ta.hs[(size_t)t * Is + i] = silu_f(g) * u;
+        return;
+    }
     const int B = a.B, np = B * a.k;
-    const bool single = gridDim.x == 1;
+    const bool single = ta.sel_blocks == 1;
     select_tokens<NS, false>(a, blockIdx.x * 4, a.zacc, a.bias, true, single ? s_pair_e : nullptr);
     if (!single) {
-        if (!arrive_last(reinterpret_cast<unsigned*>(&a.meta[M_ROUTER_CNT]), gridDim.x, &s_flag)) return;
+        if (!arrive_last(reinterpret_cast<unsigned*>(&a.meta[M_ROUTER_CNT]), ta.sel_blocks, &s_flag)) return;
         for (int p = tid; p < np; p += 256) s_pair_e[p] = ld_dev(a.topk_idx + p);
         __syncthreads();
     }
@@ -863,23 +897,24 @@ KernelPick pick_front(const FrontArgs& f, bool small_router, bool select_in_rout
         }
         lds = (size_t)a.B * a.H * 2;
     } else {
-        const int tb = f.shared_blocks > 0 && shared_tb > 0 ? tb_bucket(shared_tb) : 0;
-        switch (tb) {
-            case 0: fn = MOE_FN(front_mfma_kernel<0>); break;
-            case 1: fn = MOE_FN(front_mfma_kernel<1>); break;
-            case 2: fn = MOE_FN(front_mfma_kernel<2>); break;
-            case 4: fn = MOE_FN(front_mfma_kernel<4>); break;
-            case 8: fn = MOE_FN(front_mfma_kernel<8>); break;
-            case 16: fn = MOE_FN(front_mfma_kernel<16>); break;
-            case 32: fn = MOE_FN(front_mfma_kernel<32>); break;
-            default: fn = MOE_FN(front_mfma_kernel<64>); break;
-        }
-        lds = tb ? (size_t)shared_tb * a.H * 2 : 0;
+        return pick_front_dense(f);
     }
     return {fn, dim3(grid), dim3(256), lds};
 }
 
-KernelPick pick_topk(const RouterArgs& a) {
+KernelPick pick_front_dense(const FrontArgs& f) {
+    const void* fn;
+    switch ((f.r.B + 15) / 16) {
+        case 1: fn = MOE_FN(front_dense_kernel<1>); break;
+        case 2: fn = MOE_FN(front_dense_kernel<2>); break;
+        case 3: fn = MOE_FN(front_dense_kernel<3>); break;
+        default: fn = MOE_FN(front_dense_kernel<4>); break;
+    }
+    return {fn, dim3(f.router_blocks + f.shared_blocks), dim3(256), 0};
+}
+
+KernelPick pick_topk(const TopkArgs& t) {
+    const RouterArgs& a = t.r;
     const void* fn;
     switch (tb_bucket((a.E + 63) / 64)) {
         case 1: fn = MOE_FN(topk_bucket_kernel<1>); break;
@@ -888,7 +923,8 @@ KernelPick pick_topk(const RouterArgs& a) {
         case 8: fn = MOE_FN(topk_bucket_kernel<8>); break;
         default: fn = MOE_FN(topk_bucket_kernel<16>); break;
     }
-    return {fn, dim3((a.B + 3) / 4), dim3(256), 0};
+    const int red = t.spart ? (a.B * t.Is + 255) / 256 : 0;
+    return {fn, dim3(t.sel_blocks + red), dim3(256), 0};
 }
 
 KernelPick pick_front_split(const FrontArgs& f) {
