@@ -635,12 +635,17 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = a.H, I = a.I, B = a.B, k = a.k;
     const int nrb = (H + kDownXRows - 1) / kDownXRows;
-    const int rb = blockIdx.x % nrb, ent = blockIdx.x / nrb;
+    // grid order: the shared expert's column blocks (all B tokens, the
+    // heaviest tiles) first, then the routed entries, so that the launch's
+    // tail holds light routed tiles and the entries past n_act, which exit
+    const int rb = blockIdx.x % nrb, gent = blockIdx.x / nrb;
+    const bool routed = gent >= a.nsh;
+    const int ent = routed ? gent - a.nsh : 0;   // routed entry
+    const int sblk = routed ? 0 : gent;           // shared column block
     const int r0 = rb * kDownXRows;
     const int band = r0 + 64 * wave;
     const bool band_ok = band < H;  // H is a multiple of 64
-    const bool routed = ent < a.max_act;
-    const int ent_c = routed ? ent : 0;  // the lists are valid memory for every grid entry
+    const int ent_c = ent;  // the lists are valid memory for every grid entry
     const int nact = uni(*a.n_act);
     const int e_r = uni(a.act_e[ent_c]), off_r = uni(a.act_off[ent_c]), end_r = uni(a.act_off[ent_c + 1]);
 
@@ -661,7 +666,7 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
         hstride = I;
         dst = a.part;
     } else {
-        const int v = ent - a.max_act;
+        const int v = sblk;
         W = a.s2 + (size_t)v * I;
         ld = a.Is;
         hsrc = a.hs + (size_t)v * I;
@@ -677,7 +682,7 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
     // h rows to LDS as bf16 hi + lo pairs (when they fit) and the tokens'
     // output row offsets; called once the band's first weights are requested
     auto stage = [&]() {
-        if (tid < T) s_dsto[tid] = (routed ? a.perm[off_r + tid] : (ent - a.max_act) * B + tid) * H;
+        if (tid < T) s_dsto[tid] = (routed ? a.perm[off_r + tid] : sblk * B + tid) * H;
         if (h_lds) {
             const int I4 = I / 4;
             for (int i = tid; i < T * I4; i += 256) {
