@@ -9,7 +9,9 @@ per-forward graph is reported beside it.  Inputs are resident in HBM before
 the timed region.
 
 Workload (headline): the TP8-shard layer (H 7168, E 384, top-8 sigmoid,
-I = Is = 256) at batch 1.  A sweep at batch 16 and 64 is reported beside it.
+I = Is = 256) at batch 1.  A sweep at batch 16 and 64 is reported beside it,
+and speculative-decoding verify batches (requests of 8 tokens whose
+activations correlate, so they share experts) at 8 and 64 tokens.
 Each step uses the next of L independently drawn layers (and the next of R
 activation batches), as consecutive layers of a decode step do, so weights
 stream from HBM instead of the 256 MB Infinity Cache.
@@ -65,6 +67,8 @@ def parse():
     ap.add_argument("--batches", type=int, default=16, help="activation batches rotated per step")
     ap.add_argument("--capture", type=int, default=64, help="layer steps per captured graph")
     ap.add_argument("--sweep", type=str, default="16,64", help="extra batch sizes ('' = none)")
+    ap.add_argument("--spec", type=str, default="8,64",
+                    help="speculative-verify batch sizes, requests of 8 correlated tokens ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-only", action="store_true",
@@ -81,7 +85,7 @@ def weight_bytes(wl, n_unique: int) -> int:
     return 2 * 3 * wl.hidden * (wl.inter * n_unique + wl.shared_inter)
 
 
-def run_batch(moe, torch, synthetic, wl, layers, batch, steps, warmup, n_x, capture_len):
+def run_batch(moe, torch, synthetic, wl, layers, batch, steps, warmup, n_x, capture_len, spec=False):
     """Times `steps` layer forwards at `batch` tokens.
 
     Headline: forwards recorded into one captured graph of `capture_len`
@@ -93,10 +97,14 @@ def run_batch(moe, torch, synthetic, wl, layers, batch, steps, warmup, n_x, capt
                           wl.score_fn, 1, 1.0, 1, None)
     plan = moe.Plan(cfg)
     info = plan.info()
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(1234 + batch)
-    xs = [torch.randn(batch, wl.hidden, generator=gen, device="cuda").to(torch.bfloat16)
-          for _ in range(n_x)]
+    if spec:  # speculative-decoding verify batches: requests of 8 correlated tokens
+        xs = [synthetic.bits_to_torch_bf16(synthetic.spec_batch_x(wl, batch, offset=4096 + i * batch), "cuda")
+              for i in range(n_x)]
+    else:
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(1234 + batch)
+        xs = [torch.randn(batch, wl.hidden, generator=gen, device="cuda").to(torch.bfloat16)
+              for _ in range(n_x)]
     outs = [torch.empty_like(xs[0]) for _ in range(n_x)]
     nu = torch.zeros(max(steps, capture_len), dtype=torch.int32, device="cuda")
     L = len(layers)
@@ -151,7 +159,10 @@ def run_batch(moe, torch, synthetic, wl, layers, batch, steps, warmup, n_x, capt
     layer_s = captured_s
     bytes_mean = float(sum(weight_bytes(wl, int(u)) for u in n_unique)) / len(n_unique)
     gu_ms, gu_n = prof["gateup_routed"]
-    gu_bytes_mean = float(sum(2 * 2 * wl.hidden * wl.inter * int(u) for u in n_unique)) / len(n_unique)
+    # the routed gate/up launch also streams the shared expert's gate/up rows
+    # when the plan places them there (batch <= 4)
+    sh_gu = 2 * 2 * wl.hidden * wl.shared_inter if info.shared_gateup_in == 2 else 0
+    gu_bytes_mean = float(sum(2 * 2 * wl.hidden * wl.inter * int(u) + sh_gu for u in n_unique)) / len(n_unique)
     gu_avg_s = gu_ms * 1e-3 / gu_n
     return {
         "batch": batch,
@@ -167,7 +178,7 @@ def run_batch(moe, torch, synthetic, wl, layers, batch, steps, warmup, n_x, capt
         "hbm_frac": bytes_mean / layer_s / 1e9 / HBM_PEAK_GBPS,
         "kernel_us": {k: (v[0] * 1e3 / v[1] if v[1] else 0.0) for k, v in prof.items()},
         "gateup_routed": {"avg_us": gu_avg_s * 1e6, "GBps": gu_bytes_mean / gu_avg_s / 1e9,
-                          "bytes_per_launch": gu_bytes_mean},
+                          "bytes_per_launch": gu_bytes_mean, "with_shared_gateup": bool(sh_gu)},
     }
 
 
@@ -267,6 +278,14 @@ def main():
         sweep[str(b)] = {k: r[k] for k in ("layer_us", "layer_us_per_call", "tokens_per_s", "hbm_GBps",
                                             "hbm_frac", "unique_experts_mean", "weight_bytes_mean",
                                             "variant", "n_kernels", "kernel_us")}
+    for b in [int(s) for s in args.spec.split(",") if s.strip()]:
+        r = run_batch(moe, torch, synthetic, wl, layers, b, args.steps, args.warmup, args.batches, args.capture,
+                      spec=True)
+        log("spec-verify batch %d (%d requests x 8): %.2f us/layer captured, |U| %.1f, %.0f GB/s" % (
+            b, b // 8, r["layer_us"], r["unique_experts_mean"], r["hbm_GBps"]))
+        sweep["spec%d" % b] = {k: r[k] for k in ("layer_us", "layer_us_per_call", "tokens_per_s", "hbm_GBps",
+                                                 "hbm_frac", "unique_experts_mean", "weight_bytes_mean",
+                                                 "variant", "n_kernels", "kernel_us")}
     cpu = None
     if not args.no_cpu:
         log("cpu oracle baseline")
@@ -298,7 +317,8 @@ def main():
         "n_kernels": head["n_kernels"],
         "kernel_us": head["kernel_us"],
         "copy_GBps": cg,
-        "roofline": {"kernel": "gateup_routed", "bound": "hbm", "achieved": gu["GBps"],
+        "roofline": {"kernel": "gateup_routed" + (" + shared gate/up" if gu["with_shared_gateup"] else ""),
+                     "bound": "hbm", "achieved": gu["GBps"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gu["GBps"] / HBM_PEAK_GBPS,
                      "traffic": gateup_traffic_bytes(), "avg_us": gu["avg_us"], "bytes_per_launch": gu["bytes_per_launch"]},
         "cpu_baseline": cpu,

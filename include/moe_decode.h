@@ -121,6 +121,10 @@ typedef struct moe_decode_info {
     int32_t topk_launch;      /* resolved top-k placement: 1, 2 or 3 (see the config),
                                  0 with the single launch                              */
     size_t workspace_bytes;   /* device workspace owned by the plan                     */
+    int32_t shared_gateup_in; /* launch holding the shared expert's gate/up: 0 none (no
+                                 shared expert), 1 the router launch, 2 the routed gate/up
+                                 launch, 3 its own launch on the second stream, 4 the
+                                 single launch                                          */
 } moe_decode_info;
 
 /* Per-step counters the kernels write on the device (read back for tests). */

@@ -78,7 +78,8 @@ class Info(ctypes.Structure):
                 ("mfma_min_tokens", ctypes.c_int32), ("shared_mfma", ctypes.c_int32),
                 ("shared_stream", ctypes.c_int32), ("router_mfma", ctypes.c_int32),
                 ("single_launch", ctypes.c_int32), ("layer_grid", ctypes.c_int32),
-                ("topk_launch", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+                ("topk_launch", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+                ("shared_gateup_in", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):

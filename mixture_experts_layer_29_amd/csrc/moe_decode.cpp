@@ -89,6 +89,7 @@ struct moe_decode_plan_s {
     bool shared_stream;   // shared gate/up on the second stream instead of the front launch
     bool select_in_router;// batch <= 4: top-k + bucketing in the router's last workgroup
     bool select_in_gateup;// batch <= 4: every routed gate/up workgroup selects and buckets
+    bool shared_in_gateup;// that form also runs the shared gate/up row pairs (one per workgroup)
     bool fused;           // the whole layer as one persistent launch
     bool expert_major;    // staged down: expert-major tiles + combine launch (else output-stationary)
     size_t layer_lds;     // its dynamic LDS bytes
@@ -301,8 +302,7 @@ void fill_static_args(moe_decode_plan_s* p) {
     p->fa.router_blocks = p->select_in_gateup ? c.n_experts
                           : p->small_router     ? front_router_blocks(r, true)
                                                 : ((c.n_experts + 15) / 16) * p->dks;
-    const bool sh_sel = p->select_in_gateup && shared_in_front(p) &&
-                        c.shared_inter <= p->max_act * (c.inter / kPairsPerGemvTile);
+    const bool sh_sel = p->shared_in_gateup;
     p->sga.shared_pairs = sh_sel ? c.shared_inter : 0;
     p->fa.shared_blocks = !shared_in_front(p) || sh_sel ? 0
                           : p->select_in_gateup ? c.shared_inter
@@ -718,6 +718,8 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
         delete p;
         return fail(MOE_ERR_UNSUPPORTED, "topk_launch = 3 needs batch <= 4 with x in the LDS budget");
     }
+    p->shared_in_gateup = p->select_in_gateup && shared_in_front(p) &&
+                          c.shared_inter <= p->max_act * (c.inter / kPairsPerGemvTile);
     p->expert_major = c.batch > kDownOsMaxBatch;
     p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K, p->fused, p->expert_major,
                        p->small_router ? 1 : p->dks,
@@ -828,6 +830,8 @@ moe_status moe_decode_plan_info(moe_decode_plan_t p, moe_decode_info* info) {
     info->single_launch = p->fused ? 1 : 0;
     info->layer_grid = p->layer_grid;
     info->workspace_bytes = p->L.total;
+    info->shared_gateup_in = !has_shared(p) ? 0 : p->fused ? 4 : p->shared_stream ? 3
+                             : p->shared_in_gateup ? 2 : 1;
     return MOE_OK;
 }
 

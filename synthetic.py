@@ -30,7 +30,13 @@ SOFTMAX = 0
 SIGMOID = 1
 
 # tensor ids for sub-streams
-T_X, T_WR, T_W13, T_W2, T_S13, T_S2, T_BIAS = range(7)
+T_X, T_WR, T_W13, T_W2, T_S13, T_S2, T_BIAS, T_SPEC_BASE, T_SPEC_OWN = range(9)
+
+# Speculative-decoding verify batches: each request scores its draft tokens
+# plus one (7 drafts in the Kimi K3 article's DSpark runs, Part 3), and the
+# tokens of one request share a common direction with weight SPEC_RHO.
+SPEC_TOKENS_PER_REQUEST = 8
+SPEC_RHO = 0.5
 
 
 @dataclass(frozen=True)
@@ -79,6 +85,22 @@ def host_normal(shape, std: float, seed: int, *ids: int) -> np.ndarray:
 def token_x(wl: Workload, t: int, redraw: int = 0) -> np.ndarray:
     """Activation row for token t (redraw number ``redraw``), bf16 bits [H]."""
     return host_normal((wl.hidden,), 1.0, wl.seed, T_X, t, redraw)
+
+
+def spec_token_x(wl: Workload, t: int, redraw: int = 0, per_request: int = SPEC_TOKENS_PER_REQUEST,
+                 rho: float = SPEC_RHO) -> np.ndarray:
+    """Token t of a verify batch (requests of ``per_request`` consecutive
+    tokens): sqrt(rho) * request base + sqrt(1 - rho) * the token's own draw,
+    both ~N(0, 1), so each row keeps unit variance and rows of one request
+    have correlation rho.  bf16 bits [H]; ``redraw`` redraws the own part."""
+    H = wl.hidden
+    base = _rng(wl.seed, T_SPEC_BASE, t // per_request).standard_normal(H, dtype=np.float32)
+    own = _rng(wl.seed, T_SPEC_OWN, t, redraw).standard_normal(H, dtype=np.float32)
+    return f32_to_bf16_bits(np.float32(math.sqrt(rho)) * base + np.float32(math.sqrt(1.0 - rho)) * own)
+
+
+def spec_batch_x(wl: Workload, batch: int, offset: int = 0) -> np.ndarray:
+    return np.stack([spec_token_x(wl, offset + t) for t in range(batch)])
 
 
 def batch_x(wl: Workload, batch: int | None = None, offset: int = 0) -> np.ndarray:

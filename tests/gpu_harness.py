@@ -87,6 +87,16 @@ def gap_x(layer: DeviceLayer, shape: oracle.LayerShape, batch: int, offset: int 
     return x, n
 
 
+def gap_spec_x(layer: DeviceLayer, shape: oracle.LayerShape, batch: int, offset: int = 0):
+    """Seeded speculative-verify activations (correlated within a request) for
+    `batch` tokens, the top-k gap enforced by redrawing a token's own part."""
+    wl = layer.wl
+    x = synthetic.spec_batch_x(wl, batch, offset)
+    x, n = gapmod.enforce_gap(shape, x, layer.wr_bits, layer.bias_np,
+                              lambda t, r: synthetic.spec_token_x(wl, offset + t, r))
+    return x, n
+
+
 def run_oracle(layer: DeviceLayer, shape: oracle.LayerShape, x_bits: np.ndarray):
     z = oracle.router_logits(shape, x_bits, layer.wr_bits, layer.bias_np)
     idx, _ = oracle.select(shape, z)

@@ -134,6 +134,8 @@ def test_auto_variant(batch, variant):
     assert info.topk_launch == (2 if big else 3)
     assert info.layer_grid == 0
     assert info.shared_stream == 0
+    # batch <= 4: the shared gate/up row pairs ride in the routed gate/up launch
+    assert info.shared_gateup_in == (1 if big else 2)
     assert info.workspace_bytes > 0
     if not big:  # every gate/up tile is a GEMV tile in that form
         assert info.mfma_min_tokens == 0 and info.shared_mfma == 0
@@ -145,6 +147,7 @@ def test_auto_variant(batch, variant):
     p.destroy()
     p = moe.Plan(cfg(batch=batch, shared_stream=1))
     assert p.info().n_kernels == 4 + 2 * big and p.info().shared_stream == 1
+    assert p.info().shared_gateup_in == 3
     assert p.info().single_launch == 0
     p.destroy()
     p = moe.Plan(cfg(batch=batch, single_launch=moe.SINGLE_OFF))

@@ -12,14 +12,14 @@ import torch
 import mixture_experts_layer_29_amd as moe
 import oracle
 import synthetic
-from gpu_harness import (DeviceLayer, compare, compare_out, gap_x, make_plan, run_gpu, run_oracle,
-                         shape_of)
+from gpu_harness import (DeviceLayer, compare, compare_out, gap_spec_x, gap_x, make_plan, run_gpu,
+                         run_oracle, shape_of)
 
 pytestmark = pytest.mark.gpu
 
 
-def check(layer, shape, batch, label, offset=0, sample=None, **plan_kw):
-    x, _ = gap_x(layer, shape, batch, offset)
+def check(layer, shape, batch, label, offset=0, sample=None, spec=False, **plan_kw):
+    x, _ = (gap_spec_x if spec else gap_x)(layer, shape, batch, offset)
     plan = make_plan(layer, shape, batch, **plan_kw)
     out, idx, w, nu = run_gpu(plan, layer, x, shape)
     rows = np.arange(batch) if sample is None else np.asarray(sample)
@@ -198,6 +198,16 @@ def tp8_unit():
 @pytest.mark.parametrize("batch", [8, 16])
 def test_tp8_unit_logits(tp8_unit, batch):
     check(tp8_unit, shape_of(synthetic.TP8_UNIT), batch, "tp8 unit-logit B=%d" % batch)
+
+
+# Speculative-decoding verify batches: requests of 8 tokens whose activations
+# share a direction, so a request's tokens pick overlapping experts (fewer
+# unique experts, more tokens per expert than uniform routing at the same B).
+@pytest.mark.parametrize("batch", [8, 16, 64])
+def test_tp8_spec_verify(tp8, batch):
+    m, st, info = check(tp8, shape_of(synthetic.TP8), batch, "tp8 spec-verify B=%d" % batch, spec=True)
+    uniform = 384 * (1 - (1 - 8 / 384) ** batch)
+    assert st.n_unique < uniform, "correlated requests should share experts"
 
 
 @pytest.fixture(scope="module")
