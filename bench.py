@@ -35,13 +35,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 
-# HBM traffic of the routed gate/up kernel at batch 1 from rocprofv3 counters
-# (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the scales a 2 GiB device copy gives
-# those counters); taken on the kernel sources with these SHA-1s and reported
-# only while the sources are unchanged (profiles/*hbm_traffic.md).
-GATEUP_TRAFFIC = {"fetch_kib": 28777.6, "write_kib": 64.0, "fetch_scale": 2.0, "write_scale": 1.0,
-                  "sources": {"moe_device.h": "890e32cc8e28f6e4e6fd990f8b831643ff96583f",
-                              "moe_kernels.hip": "294b925ee863e296884ba17f5f0e7751692fa7a1"}}
+# HBM traffic of the gate/up launch at batch 1 (routed gate/up + the shared
+# expert's gate/up rows) from rocprofv3 counters (FETCH_SIZE x 2.0 and
+# WRITE_SIZE x 1.0, the scales a 2 GiB device copy gives those counters); taken
+# on the kernel sources with these SHA-1s and reported only while the sources
+# are unchanged (profiles/gateup_select_tp8shard_b1_hbm_traffic.md).
+GATEUP_TRAFFIC = {"fetch_kib": 32468.2, "write_kib": 72.4, "fetch_scale": 2.0, "write_scale": 1.0,
+                  "sources": {"moe_device.h": "6711847b4044062274d1023d8aadb2594466c613",
+                              "moe_kernels.hip": "48c885c006f225a20f16bcad0acfe377699f265e"}}
 
 
 def gateup_traffic_bytes():
