@@ -196,7 +196,7 @@ __device__ __forceinline__ void wg_rows_dot(const uint16_t* const (&w)[NR], cons
         for (int q = 0; q < Q; ++q) {
             const int u = u0 + 256 * q + tid;
 #pragma unroll
-            for (int r = 0; r < NR; ++r) wv[q][r] = u < units ? ld16(w[r] + u * 8) : zero;
+            for (int r = 0; r < NR; ++r) wv[q][r] = u < units ? ld16_stream(w[r] + u * 8) : zero;
         }
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
         for (int q = 0; q < Q; ++q) {
             const int u = 256 * q + tid;
 #pragma unroll
-            for (int r = 0; r < 2; ++r) swv[q][r] = u < units ? ld16(srow[r] + u * 8) : zero;
+            for (int r = 0; r < 2; ++r) swv[q][r] = u < units ? ld16_stream(srow[r] + u * 8) : zero;
 #pragma unroll
             for (int t = 0; t < TB; ++t)
                 sxv[q][t] = (u < units && t < a.B) ? ld16(sg.x + (size_t)t * sg.H + u * 8) : zero;
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
         for (int u = 256 * Q + tid; u < units; u += 256)
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const u32x4 w = ld16(srow[r] + u * 8);
+                const u32x4 w = ld16_stream(srow[r] + u * 8);
 #pragma unroll
                 for (int t = 0; t < TB; ++t)
                     if (t < a.B) acc[r][t] = dot8(w, ld16(sg.x + (size_t)t * sg.H + u * 8), acc[r][t]);
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(256) void down_os_kernel(DownArgs a) {
             if (ent < total) {
                 const uint16_t* w = w_of(ent, eid0[c0 + ce]);
 #pragma unroll
-                for (int q = 0; q < NQ; ++q) buf[ce][q] = ld16(w + 8 * LPR * q);
+                for (int q = 0; q < NQ; ++q) buf[ce][q] = ld16_stream(w + 8 * LPR * q);
             }
         }
     };
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(256) void down_os_kernel(DownArgs a) {
             if (ent < total) {
                 const uint16_t* w = w_of(ent, ent < nact ? uni(s_acte[ent]) : 0);
 #pragma unroll
-                for (int q = 0; q < NQ; ++q) buf[ce][q] = ld16(w + 8 * LPR * q);
+                for (int q = 0; q < NQ; ++q) buf[ce][q] = ld16_stream(w + 8 * LPR * q);
             }
         }
     };
@@ -712,7 +712,7 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
                 const bool ok = band_ok && q0 + q < P;
 #pragma unroll
                 for (int u = 0; u < NQ; ++u)
-                    w[q][u] = ok ? ld16(W + (size_t)row * ld + 8 * (c + LPR * u)) : zero;
+                    w[q][u] = ok ? ld16_stream(W + (size_t)row * ld + 8 * (c + LPR * u)) : zero;
             }
         };
         // two register buffers; the batch loop is unrolled, so they alternate
@@ -769,7 +769,7 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
             for (int st = 0; st < NSC; ++st)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    A[st][g] = band_ok ? ld16(arow + (size_t)16 * g * ld + c0 + 32 * st) : zero;
+                    A[st][g] = band_ok ? ld16_stream(arow + (size_t)16 * g * ld + c0 + 32 * st) : zero;
             if (c0 == 0) stage();
 #pragma unroll
             for (int st = 0; st < NSC; ++st) {
