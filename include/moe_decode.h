@@ -73,7 +73,8 @@ typedef struct moe_decode_config {
     const float* router_bias;/* device fp32 [E] added to the logits, or NULL          */
     int32_t force_variant;   /* moe_variant                                           */
     int32_t mfma_min_tokens; /* SPLIT_K: token count from which an expert uses MFMA
-                                tiles; 0 = library default                           */
+                                tiles; 0 = library default (5, or less where the
+                                GEMV tiles' activation staging does not fit)         */
     int32_t shared_stream;   /* 0: the shared expert's gate/up runs in trailing
                                 workgroups of the router launch (overlap without a
                                 second queue); 1: on the plan's second stream,

@@ -140,8 +140,8 @@ def test_auto_variant(batch, variant):
     if not big:  # every gate/up tile is a GEMV tile in that form
         assert info.mfma_min_tokens == 0 and info.shared_mfma == 0
     elif variant == moe.VARIANT_SPLIT_K:
-        assert info.mfma_min_tokens == 4
-        assert info.shared_mfma == (1 if batch >= 4 else 0)
+        assert info.mfma_min_tokens == 5
+        assert info.shared_mfma == (1 if batch >= 5 else 0)
     else:
         assert info.mfma_min_tokens == 0 and info.shared_mfma == 0
     p.destroy()

@@ -225,19 +225,22 @@ def test_tp8_zipf_skew(tp8_zipf):
 def test_tp8_identical_tokens_route_together(tp8, B, single, topk_launch):
     """Every token identical: the k selected experts each get all B tokens.
     At B = 4 the default staged form runs them on GEMV tiles of 4 tokens; with
-    the selection in the router (topk_launch 1), inside the single launch and
-    at B = 16 they go through the split-K MFMA tiles."""
+    the selection in the router (topk_launch 1) or inside the single launch,
+    given an MFMA threshold of 4 tokens, and at B = 16 (default threshold) they
+    go through the split-K MFMA tiles."""
     shape = shape_of(synthetic.TP8)
     x1, _ = gap_x(tp8, shape, 1, offset=500)
     x = np.repeat(x1, B, axis=0)
-    plan = make_plan(tp8, shape, B, single_launch=single, topk_launch=topk_launch)
+    gemv_form = B <= 4 and not single and topk_launch == 0
+    kw = {} if gemv_form or B > 4 else dict(mfma_min_tokens=4)
+    plan = make_plan(tp8, shape, B, single_launch=single, topk_launch=topk_launch, **kw)
     out, idx, w, nu = run_gpu(plan, tp8, x, shape)
     out64, idx_o, w_o = run_oracle(tp8, shape, x)
     compare(out, idx, w, out64, idx_o, w_o, "identical tokens")
     assert plan.info().single_launch == (1 if single else 0)
     st = plan.stats()
     assert nu == 8
-    if B <= 4 and not single and topk_launch == 0:
+    if gemv_form:
         assert st.mfma_tiles == 0 and st.gemv_tiles == 8 * (shape.inter // 4)
     else:
         assert st.mfma_tiles > 0 and st.gemv_tiles == 0
