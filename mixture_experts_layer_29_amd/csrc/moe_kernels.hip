@@ -820,25 +820,37 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
 }
 
 // out[t][r] = bf16( sum_j w[t][j] * part[t*k+j][r] + sum_sb part_s[sb][t][r] (+ x) ),
-// summed in that fixed order; four rows per thread.
-__global__ __launch_bounds__(256) void combine_kernel(DownXArgs a) {
+// summed in that fixed order; four rows per thread.  KB >= k: the k partial
+// rows of a token are requested in one round (addresses past k clamped, their
+// terms skipped).
+template <int KB>
+__global__ __launch_bounds__(128) void combine_kernel(DownXArgs a) {
     const int H = a.H, k = a.k, B = a.B;
-    const int i4 = blockIdx.x * 256 + threadIdx.x;
+    const int i4 = blockIdx.x * 128 + threadIdx.x;
     if (i4 >= B * H / 4) return;
     const int t = (4 * i4) / H, r = 4 * i4 - t * H;
+    float4 y[KB];
+    float w[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+        const int p = t * k + (j < k ? j : k - 1);
+        y[j] = *reinterpret_cast<const float4*>(a.part + (size_t)p * H + r);
+        w[j] = a.topk_w[p];
+    }
+    uint2 xb = uint2{0, 0};
+    if (a.add_residual) xb = *reinterpret_cast<const uint2*>(a.x + (size_t)t * H + r);
     float4 v = float4{0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-        const int p = t * k + j;
-        const float w = a.topk_w[p];
-        const float4 y = *reinterpret_cast<const float4*>(a.part + (size_t)p * H + r);
-        v.x += w * y.x; v.y += w * y.y; v.z += w * y.z; v.w += w * y.w;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+        if (j < k) {
+            v.x += w[j] * y[j].x; v.y += w[j] * y[j].y; v.z += w[j] * y[j].z; v.w += w[j] * y[j].w;
+        }
     }
     for (int sb = 0; sb < a.nsh; ++sb) {
-        const float4 y = *reinterpret_cast<const float4*>(a.part_s + ((size_t)sb * B + t) * H + r);
-        v.x += y.x; v.y += y.y; v.z += y.z; v.w += y.w;
+        const float4 ys = *reinterpret_cast<const float4*>(a.part_s + ((size_t)sb * B + t) * H + r);
+        v.x += ys.x; v.y += ys.y; v.z += ys.z; v.w += ys.w;
     }
     if (a.add_residual) {
-        const uint2 xb = *reinterpret_cast<const uint2*>(a.x + (size_t)t * H + r);
         v.x += bf16_lo(xb.x); v.y += bf16_hi(xb.x); v.z += bf16_lo(xb.y); v.w += bf16_hi(xb.y);
     }
     const uint32_t o0 = f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
@@ -1041,7 +1053,15 @@ KernelPick pick_down_os(const DownArgs& a) {
 size_t down_os_lds_bytes(int B, int k, int I, int Is) { return ((size_t)B * k + (size_t)B * (Is / I)) * I * 4; }
 
 KernelPick pick_combine(const DownXArgs& a) {
-    return {MOE_FN(combine_kernel), dim3((a.B * a.H / 4 + 255) / 256), dim3(256), 0};
+    const void* f;
+    switch (tb_bucket(a.k)) {
+        case 1: f = MOE_FN(combine_kernel<1>); break;
+        case 2: f = MOE_FN(combine_kernel<2>); break;
+        case 4: f = MOE_FN(combine_kernel<4>); break;
+        case 8: f = MOE_FN(combine_kernel<8>); break;
+        default: f = MOE_FN(combine_kernel<16>); break;
+    }
+    return {f, dim3((a.B * a.H / 4 + 127) / 128), dim3(128), 0};
 }
 
 KernelPick pick_down_x(const DownXArgs& a) {
