@@ -40,9 +40,9 @@ HBM_PEAK_GBPS = 8000.0
 # WRITE_SIZE x 1.0, the scales a 2 GiB device copy gives those counters); taken
 # on the kernel sources with these SHA-1s and reported only while the sources
 # are unchanged (profiles/gateup_select_tp8shard_b1_hbm_traffic.md).
-GATEUP_TRAFFIC = {"fetch_kib": 32468.2, "write_kib": 72.4, "fetch_scale": 2.0, "write_scale": 1.0,
-                  "sources": {"moe_device.h": "6711847b4044062274d1023d8aadb2594466c613",
-                              "moe_kernels.hip": "48c885c006f225a20f16bcad0acfe377699f265e"}}
+GATEUP_TRAFFIC = {"fetch_kib": 32422.2, "write_kib": 72.3, "fetch_scale": 2.0, "write_scale": 1.0,
+                  "sources": {"moe_device.h": "51141d85bab0ef7fc4787baded9ddfdde4a0453b",
+                              "moe_kernels.hip": "1fd449da8cd6addb21dcdc0f2bf80986cfe616c7"}}
 
 
 def gateup_traffic_bytes():
@@ -234,7 +234,7 @@ def cpu_baseline(torch, synthetic, wl, layer, budget_s: float) -> dict:
 
     ntok = max(threads, 8)
     dt = sample(ntok, 0)
-    ntok2 = int(max(ntok, min(4096, ntok * budget_s / max(dt, 1e-3) * 0.8)))
+    ntok2 = int(max(ntok, min(16384, ntok * budget_s / max(dt, 1e-3) * 0.8)))
     ntok2 = (ntok2 + threads - 1) // threads * threads
     dt2 = sample(ntok2, 1)
     return {"value": ntok2 / dt2, "unit": "tokens/s", "cores": threads, "kind": "oracle",
