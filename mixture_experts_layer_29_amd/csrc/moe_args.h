@@ -54,7 +54,8 @@ struct RouterArgs {
     int32_t* topk_idx;      // [B][k]
     float* topk_w;          // [B][k]
     int32_t* meta;
-    int32_t* act_e;         // [max_act]   active expert ids, ascending
+    int32_t* act_e;         // [max_act]   active expert ids (ascending; above batch 4 those with
+                            //             >= mfma_min_tokens tokens first, each class ascending)
     int32_t* act_off;       // [max_act+1] slot offsets of each active expert
     int32_t* perm;          // [B*k]       slot -> pair id (token*k + j)
     int32_t H, E, k, B;

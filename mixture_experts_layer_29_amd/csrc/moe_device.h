@@ -458,30 +458,48 @@ __device__ __forceinline__ void bucket_block(const RouterArgs& a, const int32_t*
     __syncthreads();
     // (an invalid id leaves ctot < npairs; bucket_meta then publishes an empty list)
 
+    // Entries (and their slot ranges) in two classes: experts with at least
+    // mfma_min_tokens tokens first, then the rest, each by ascending id.  The
+    // grids of the staged gate/up and down launches follow the entry order, so
+    // the heavy entries are dispatched first and the launches end on light ones.
     constexpr int CH = kMaxExperts / 256;  // bins per thread
-    int cnt[CH], csum = 0, fsum = 0;
+    int cnt[CH], hc = 0, hf = 0, lc = 0, lf = 0;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int bin = tid * CH + c;
         cnt[c] = (bin < E) ? s_cnt[bin] : 0;
-        csum += cnt[c];
-        fsum += cnt[c] > 0 ? 1 : 0;
+        const bool hot = a.mfma_min_tokens > 0 && cnt[c] >= a.mfma_min_tokens;
+        hc += hot ? cnt[c] : 0;
+        hf += hot ? 1 : 0;
+        lc += hot ? 0 : cnt[c];
+        lf += (!hot && cnt[c] > 0) ? 1 : 0;
     }
-    int cex, fex, ctot, ftot;
-    block_scan2(csum, fsum, s_tmp, cex, fex, ctot, ftot);
+    int hcx, hfx, hct, hft, lcx, lfx, lct, lft;
+    block_scan2(hc, hf, s_tmp, hcx, hfx, hct, hft);
+    block_scan2(lc, lf, s_tmp, lcx, lfx, lct, lft);
+    lcx += hct;  // the light entries' slots and list positions follow the heavy ones
+    lfx += hft;
+    const int ctot = hct + lct, ftot = hft + lft;
     int nm = 0;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int bin = tid * CH + c;
         if (bin < E) {
+            const bool hot = a.mfma_min_tokens > 0 && cnt[c] >= a.mfma_min_tokens;
+            const int cex = hot ? hcx : lcx, fex = hot ? hfx : lfx;
             s_cnt[bin] = cex;  // becomes the bucket offset
             if (cnt[c] > 0) {
                 st_dev(a.act_e + fex, bin);
                 st_dev(a.act_off + fex, cex);
-                if (a.mfma_min_tokens > 0 && cnt[c] >= a.mfma_min_tokens) ++nm;
-                ++fex;
+                if (hot) {
+                    ++nm;
+                    ++hfx;
+                } else {
+                    ++lfx;
+                }
             }
-            cex += cnt[c];
+            if (hot) hcx += cnt[c];
+            else lcx += cnt[c];
         }
     }
     if (nm) atomicAdd(s_nmfma, nm);
