@@ -917,6 +917,114 @@ __device__ __forceinline__ bool mfma_gateup_tile(const GateUpArgs& a, const uint
 }
 
 
+// Split-K MFMA tile of the staged gate/up launch (batch > 4): the same tile
+// as mfma_gateup_tile<4> (64 row pairs x one K slice x T <= 64 tokens, fp32
+// partials to g_acc, the last of the ksplit tiles applies SiLU*up), but a wave
+// requests all gate and up weights of its slice (up to kMfmaChunk steps of 32)
+// in one round, and the tokens' activations for the slice are staged in LDS
+// (rows padded by 8 elements against bank conflicts) while the weights stream.
+constexpr int kMfmaChunk = 14;                    // K steps of 32 per round (the TP8 shape's slice)
+constexpr int kMfmaXLd = kMfmaChunk * 32 + 8;     // LDS row stride of staged x (elements)
+__host__ __device__ constexpr size_t mfma_tile_lds_bytes() { return (size_t)kMaxBatch * kMfmaXLd * 2; }
+
+__device__ __forceinline__ bool mfma_gateup_tile_lds(const GateUpArgs& a, const uint16_t* W, int entry, int off,
+                                                     int T, int local, uint16_t* s_x) {
+    __shared__ int s_tk[kMaxBatch];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H, n = a.n;
+    const int nrb = n / kPairsPerMfmaTile;
+    const int rb = local / a.ksplit, ks = local % a.ksplit;
+    if (rb >= nrb) return false;
+    const int i0 = rb * kPairsPerMfmaTile + wave * 16;
+    const int kbeg = ks * a.kslice;
+    const int nsteps = min(a.kslice, H - kbeg) >> 5;
+    const int tl = lane & 15, kq = lane >> 4;
+    const int NT = (T + 15) >> 4;
+    const uint16_t* gr = W + (size_t)(i0 + tl) * H + kbeg + 8 * kq;
+    const uint16_t* ur = W + (size_t)(n + i0 + tl) * H + kbeg + 8 * kq;
+    const u32x4 zero = u32x4{0, 0, 0, 0};
+    f32x4 cg[4], cu[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) { cg[tt] = f32x4{0, 0, 0, 0}; cu[tt] = f32x4{0, 0, 0, 0}; }
+    for (int c0 = 0; c0 < nsteps; c0 += kMfmaChunk) {
+        const int ns = min(kMfmaChunk, nsteps - c0);
+        u32x4 Ag[kMfmaChunk], Au[kMfmaChunk];
+#pragma unroll
+        for (int u = 0; u < kMfmaChunk; ++u) {
+            const bool ok = u < ns;
+            Ag[u] = ok ? ld16_stream(gr + 32 * (c0 + u)) : zero;
+            Au[u] = ok ? ld16_stream(ur + 32 * (c0 + u)) : zero;
+        }
+        // stage x[T][ns * 32] of this chunk: token ids first, then this
+        // thread's units (at most 64 * 14 * 4 / 256 <= 16) in rounds of 8
+        if (c0 == 0 && tid < T) s_tk[tid] = ld_dev(a.perm + off + tid) / a.pair_div;
+        __syncthreads();  // token ids in; the previous chunk's reads of s_x done
+        const int upr = ns * 4;  // 16-byte units per token row of the chunk
+        for (int q0 = 0; q0 < 16; q0 += 8) {  // two rounds of 8 units: registers stay for the weights
+            if (256 * q0 >= T * upr) break;
+            u32x4 xv[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = tid + 256 * (q0 + q);
+                const int j = idx / upr, uu = idx - j * upr;
+                xv[q] = idx < T * upr ? ld16(a.x + (size_t)s_tk[j < T ? j : 0] * H + kbeg + 32 * c0 + 8 * uu) : zero;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = tid + 256 * (q0 + q);
+                const int j = idx / upr, uu = idx - j * upr;
+                if (idx < T * upr) st16(s_x + j * kMfmaXLd + 8 * uu, xv[q]);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kMfmaChunk; ++u) {
+            if (u < ns) {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    if (tt < NT) {
+                        const int j = tt * 16 + tl;
+                        const u32x4 xb = j < T ? ld16(s_x + j * kMfmaXLd + 32 * u + 8 * kq) : zero;
+                        const bf16x8 Bx = __builtin_bit_cast(bf16x8, xb);
+                        cg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Ag[u]), Bx,
+                                                                         cg[tt], 0, 0, 0);
+                        cu[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Au[u]), Bx,
+                                                                         cu[tt], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+    // D layout: lane holds rows 4*(lane/16)+r, column (token) lane%16
+    const int n2 = 2 * n;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int j = tt * 16 + tl;
+        if (tt < NT && j < T) {
+            float* gp = a.g_acc + (size_t)(off + j) * n2 + i0 + 4 * kq;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                atomicAdd(gp + r, cg[tt][r]);
+                atomicAdd(gp + n + r, cu[tt][r]);
+            }
+        }
+    }
+    __shared__ int s_flag;
+    if (!arrive_last(&a.tile_cnt[entry * nrb + rb], (unsigned)a.ksplit, &s_flag)) return true;
+    const int rows = kPairsPerMfmaTile;
+    for (int idx = tid; idx < rows * T; idx += 256) {
+        const int j = idx / rows, i = rb * rows + idx % rows;
+        float* gp = a.g_acc + (size_t)(off + j) * n2;
+        const float g = ld_dev(gp + i), u = ld_dev(gp + n + i);
+        st_dev(a.h + (size_t)(off + j) * n + i, silu_f(g) * u);
+        st_dev(gp + i, 0.0f);
+        st_dev(gp + n + i, 0.0f);
+    }
+    if (tid == 0) st_dev(a.tile_cnt + entry * nrb + rb, 0u);
+    return true;
+}
+
+
 // ---------------------------------------------------------------------------
 // down
 // ---------------------------------------------------------------------------

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
             if (threadIdx.x == 0 && local == 0) atomicOr(&a.meta[M_ERR], ERR_TILE);
             return;
         }
-        mfma_gateup_tile<4>(a, W, entry, off, T, local);
+        mfma_gateup_tile_lds(a, W, entry, off, T, local, s_x);
     } else {
         if (T > TB) {
             if (threadIdx.x == 0 && local == 0) atomicOr(&a.meta[M_ERR], ERR_TILE);
@@ -984,7 +984,9 @@ KernelPick pick_gateup(const GateUpArgs& a, int max_entries, int gemv_tokens) {
         default: MOE_GU(64) break;
     }
 #undef MOE_GU
-    return {f, dim3(max_entries * a.tiles_per_expert), dim3(256), (size_t)gemv_tokens * a.H * 2};
+    size_t lds = (size_t)gemv_tokens * a.H * 2;
+    if (mf) lds = std::max(lds, mfma_tile_lds_bytes());  // the MFMA tiles' staged activations
+    return {f, dim3(max_entries * a.tiles_per_expert), dim3(256), lds};
 }
 
 // Output rows per down row block of the single launch for intermediate size I.
