@@ -10,8 +10,9 @@ the timed region.
 
 Workload (headline): the TP8-shard layer (H 7168, E 384, top-8 sigmoid,
 I = Is = 256) at batch 1.  A sweep at batch 16 and 64 is reported beside it,
-and speculative-decoding verify batches (requests of 8 tokens whose
-activations correlate, so they share experts) at 8 and 64 tokens.
+speculative-decoding verify batches (requests of 8 tokens whose activations
+correlate, so they share experts) at 8 and 64 tokens, and a batch of 64 with
+Zipf(1.1)-skewed routing (a per-expert logit bias on the same layers).
 Each step uses the next of L independently drawn layers (and the next of R
 activation batches), as consecutive layers of a decode step do, so weights
 stream from HBM instead of the 256 MB Infinity Cache.
@@ -41,8 +42,8 @@ HBM_PEAK_GBPS = 8000.0
 # on the kernel sources with these SHA-1s and reported only while the sources
 # are unchanged (profiles/gateup_select_tp8shard_b1_hbm_traffic.md).
 GATEUP_TRAFFIC = {"fetch_kib": 32422.2, "write_kib": 72.3, "fetch_scale": 2.0, "write_scale": 1.0,
-                  "sources": {"moe_device.h": "51141d85bab0ef7fc4787baded9ddfdde4a0453b",
-                              "moe_kernels.hip": "1fd449da8cd6addb21dcdc0f2bf80986cfe616c7"}}
+                  "sources": {"moe_device.h": "a68d097bde31ec7214ddf8816a5abe073a9e7b21",
+                              "moe_kernels.hip": "c8048b744f790bc320928c635be84792bb0b4162"}}
 
 
 def gateup_traffic_bytes():
@@ -70,6 +71,8 @@ def parse():
     ap.add_argument("--sweep", type=str, default="16,64", help="extra batch sizes ('' = none)")
     ap.add_argument("--spec", type=str, default="8,64",
                     help="speculative-verify batch sizes, requests of 8 correlated tokens ('' = none)")
+    ap.add_argument("--zipf", type=str, default="64",
+                    help="batch sizes with Zipf(1.1)-skewed routing (a per-expert logit bias) ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-only", action="store_true",
@@ -86,7 +89,7 @@ def weight_bytes(wl, n_unique: int) -> int:
     return 2 * 3 * wl.hidden * (wl.inter * n_unique + wl.shared_inter)
 
 
-def run_batch(moe, torch, synthetic, wl, layers, batch, steps, warmup, n_x, capture_len, spec=False):
+def run_batch(moe, torch, synthetic, wl, layers, batch, steps, warmup, n_x, capture_len, spec=False, bias=None):
     """Times `steps` layer forwards at `batch` tokens.
 
     Headline: forwards recorded into one captured graph of `capture_len`
@@ -95,7 +98,7 @@ def run_batch(moe, torch, synthetic, wl, layers, batch, steps, warmup, n_x, capt
     Then a pass reading back each step's |U|, and a pass with per-kernel HIP
     events (eager launches)."""
     cfg = moe.make_config(wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter, batch,
-                          wl.score_fn, 1, 1.0, 1, None)
+                          wl.score_fn, 1, 1.0, 1, bias)
     plan = moe.Plan(cfg)
     info = plan.info()
     if spec:  # speculative-decoding verify batches: requests of 8 correlated tokens
@@ -285,6 +288,16 @@ def main():
         log("spec-verify batch %d (%d requests x 8): %.2f us/layer captured, |U| %.1f, %.0f GB/s" % (
             b, b // 8, r["layer_us"], r["unique_experts_mean"], r["hbm_GBps"]))
         sweep["spec%d" % b] = {k: r[k] for k in ("layer_us", "layer_us_per_call", "tokens_per_s", "hbm_GBps",
+                                                 "hbm_frac", "unique_experts_mean", "weight_bytes_mean",
+                                                 "variant", "n_kernels", "kernel_us")}
+    zb = synthetic.zipf_bias(synthetic.TP8_ZIPF)
+    zbias = torch.from_numpy(zb).cuda()
+    for b in [int(s) for s in args.zipf.split(",") if s.strip()]:
+        r = run_batch(moe, torch, synthetic, wl, layers, b, args.steps, args.warmup, args.batches, args.capture,
+                      bias=zbias)
+        log("zipf-skewed batch %d: %.2f us/layer captured, |U| %.1f, %.0f GB/s" % (
+            b, r["layer_us"], r["unique_experts_mean"], r["hbm_GBps"]))
+        sweep["zipf%d" % b] = {k: r[k] for k in ("layer_us", "layer_us_per_call", "tokens_per_s", "hbm_GBps",
                                                  "hbm_frac", "unique_experts_mean", "weight_bytes_mean",
                                                  "variant", "n_kernels", "kernel_us")}
     cpu = None
