@@ -80,8 +80,10 @@ typedef struct moe_decode_config {
                                 second queue); 1: on the plan's second stream,
                                 forked before the router and joined before the down
                                 projection                                           */
-    int32_t topk_launch;     /* batch <= 4 only.  0: default (3 where it applies,
-                                else 1); 1: top-k and bucketing in the router
+    int32_t topk_launch;     /* batch <= 4 only.  0: default (3 where it applies
+                                and the routed gate/up grid is one generation of
+                                workgroups, at most 512 -- batch 1 of the TP8
+                                shape -- else 1); 1: top-k and bucketing in the router
                                 launch's last workgroup to arrive; 2: in a launch of
                                 their own after the router; 3: in every routed
                                 gate/up workgroup, each deriving the same work lists

@@ -60,6 +60,7 @@ moe_status fail(moe_status st, const char* fmt, ...) {
 constexpr int kDefaultMfmaMin = 5;
 constexpr int kMaxProfiledForwards = 1024;
 constexpr int kSmallRouterMaxBatch = 4;
+constexpr size_t kSelectGateupMaxTiles = 512;  // gate/up workgroups of one generation (2 per CU x 256 CUs)
 constexpr size_t kSmallRouterLds = 56 * 1024;
 
 constexpr size_t kLayerLds = 56 * 1024;
@@ -699,13 +700,20 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
             return fail(MOE_ERR_UNSUPPORTED, "single_launch = 2: %s", why);
         }
     }
-    // Batch <= 4: the selection by default runs in every routed gate/up
-    // workgroup (topk_launch 3).  That form runs every tile as a GEMV tile, so
+    // Batch <= 4: the selection can run in every routed gate/up workgroup
+    // (topk_launch 3).  That form runs every tile as a GEMV tile, so
     // with the library's MFMA threshold it turns MFMA tiles off; a threshold
     // the caller set that could reach MFMA tiles keeps the selection in the
     // router's last workgroup (topk_launch 1) unless 3 is asked for.
+    // By default that form is taken only while the gate/up grid is one
+    // generation of workgroups (two per CU): every workgroup pays the
+    // selection before its weights, so a second generation pays it again.
+    // Measured on MI355X (TP8 shard): batch 1 (512 workgroups) 35.6 us in that
+    // form vs 39.0 us selecting in the router; batch 2 61.0 vs 58.8 us; batch 4
+    // 105.8 vs 93.2 us.
+    const bool one_generation = (size_t)p->max_act * (c.inter / kPairsPerGemvTile) <= kSelectGateupMaxTiles;
     p->select_in_gateup = false;
-    if (!p->fused && p->small_router && (c.topk_launch == 0 || c.topk_launch == 3)) {
+    if (!p->fused && p->small_router && (c.topk_launch == 3 || (c.topk_launch == 0 && one_generation))) {
         const bool gemv_only = !p->shared_mfma && (p->mfma_min == 0 || p->mfma_min > c.batch);
         if (gemv_only || c.mfma_min_tokens == 0) {
             p->select_in_gateup = true;

@@ -124,20 +124,24 @@ def test_auto_variant(batch, variant):
     p = moe.Plan(cfg(batch=batch))
     info = p.info()
     assert info.variant == variant
-    # batch <= 4: router, gate/up (selecting for itself, shared gate/up
-    # included), down; above: router MFMA launch (+ shared gate/up), top-k
-    # launch, routed gate/up, expert-major down, combine
+    # batch 1: router, gate/up (selecting for itself, shared gate/up
+    # included), down -- its gate/up grid (8 experts x 64 tiles) is one
+    # generation of workgroups; batch 2-4: router (+ selection in its last
+    # workgroup, + shared gate/up), gate/up, down; above: router MFMA launch
+    # (+ shared gate/up), top-k launch, routed gate/up, expert-major down,
+    # combine
     big = 1 if batch > 4 else 0
+    sel_gu = batch == 1
     assert info.router_mfma == big
     assert info.single_launch == 0
     assert info.n_kernels == 3 + 2 * big
-    assert info.topk_launch == (2 if big else 3)
+    assert info.topk_launch == (2 if big else 3 if sel_gu else 1)
     assert info.layer_grid == 0
     assert info.shared_stream == 0
-    # batch <= 4: the shared gate/up row pairs ride in the routed gate/up launch
-    assert info.shared_gateup_in == (1 if big else 2)
+    # batch 1: the shared gate/up row pairs ride in the routed gate/up launch
+    assert info.shared_gateup_in == (2 if sel_gu else 1)
     assert info.workspace_bytes > 0
-    if not big:  # every gate/up tile is a GEMV tile in that form
+    if sel_gu:  # every gate/up tile is a GEMV tile in that form
         assert info.mfma_min_tokens == 0 and info.shared_mfma == 0
     elif variant == moe.VARIANT_SPLIT_K:
         assert info.mfma_min_tokens == 5
@@ -189,8 +193,13 @@ def test_topk_launch_policy(batch):
         i = p.info()
         p.destroy()
         return i
+    # by default every gate/up workgroup selects for itself only while the
+    # gate/up grid is one generation (batch 1 at this shape)
+    default_tl = 3 if batch == 1 else 1
     i = info()
-    assert i.topk_launch == 3 and i.n_kernels == 3 and i.mfma_min_tokens == 0 and i.shared_mfma == 0
+    assert i.topk_launch == default_tl and i.n_kernels == 3 and i.shared_mfma == 0
+    if batch == 1:
+        assert i.mfma_min_tokens == 0
     i = info(topk_launch=3, shared_stream=1)
     assert i.topk_launch == 3 and i.n_kernels == 4
     i = info(topk_launch=1)
@@ -202,7 +211,7 @@ def test_topk_launch_policy(batch):
     assert i.topk_launch == 1 and i.mfma_min_tokens == 1 and i.shared_mfma == 1
     # one it cannot reach does not
     i = info(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=batch + 1)
-    assert i.topk_launch == 3 and i.shared_mfma == 0
+    assert i.topk_launch == default_tl and i.shared_mfma == 0
     i = info(single_launch=moe.SINGLE_REQUIRED)
     assert i.topk_launch == 0 and i.n_kernels == 1
 
