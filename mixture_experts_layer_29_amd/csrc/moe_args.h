@@ -39,7 +39,6 @@ constexpr int kPairsPerMfmaTile = 64;
 constexpr int kMaxGemvUnits = 16;  // 16-byte units per lane held in registers by a GEMV wave
 constexpr int kGemvLdsBytes = 60 * 1024;  // x staging budget of a GEMV workgroup
 constexpr int kXStage = 4;                 // x units per thread requested ahead of a GEMV's weights
-constexpr int kRouterRowsPerMfmaTile = 64;
 constexpr int kDownHStage = 32 * 1024;  // LDS bytes for a staged batch of h rows in down
 
 // Router + top-k + routing weights + bucketing.  Batches up to 4 use one
@@ -53,7 +52,6 @@ struct RouterArgs {
     float* z;               // fp32 [B][E] logits (workspace)
     float* zacc;            // fp32 [nzpart][B][E] partial logits for a later top-k launch
     int32_t nzpart;         // partial slices in zacc (1: full sums)
-    int32_t ksplit, kslice; // MFMA gate/up tiles: K splits and K elements per split
     int32_t* topk_idx;      // [B][k]
     float* topk_w;          // [B][k]
     int32_t* meta;
@@ -222,7 +220,7 @@ KernelPick pick_init(const InitArgs& a);
 // and bucketing follow in pick_topk's launch.  shared_tb: 0 when the shared
 // expert uses MFMA tiles, else its GEMV token count.
 KernelPick pick_front(const FrontArgs& f, bool small_router, bool select_in_router, int shared_tb);
-int front_router_blocks(const RouterArgs& a, bool small_router);
+int front_router_blocks(const RouterArgs& a);  // batch <= 4: four router rows per workgroup
 KernelPick pick_topk(const TopkArgs& a);
 // Dense split-K front (router + shared gate/up partials) for batch > 4.
 KernelPick pick_front_dense(const FrontArgs& f);

@@ -239,8 +239,6 @@ void fill_static_args(moe_decode_plan_s* p) {
     r.z = at<float>(p, p->L.z);
     r.zacc = at<float>(p, p->L.zacc);
     r.nzpart = p->small_router ? 1 : p->dks;
-    r.ksplit = p->ksplit;
-    r.kslice = p->kslice;
     r.topk_idx = at<int32_t>(p, p->L.topk_idx);
     r.topk_w = at<float>(p, p->L.topk_w);
     r.meta = at<int32_t>(p, p->L.meta);
@@ -305,7 +303,7 @@ void fill_static_args(moe_decode_plan_s* p) {
     // launch (one per workgroup, during the selection) when it has enough
     // workgroups, else in the front, one pair per workgroup.
     p->fa.router_blocks = p->select_in_gateup ? c.n_experts
-                          : p->small_router     ? front_router_blocks(r, true)
+                          : p->small_router     ? front_router_blocks(r)
                                                 : ((c.n_experts + 15) / 16) * p->dks;
     const bool sh_sel = p->shared_in_gateup;
     p->sga.shared_pairs = sh_sel ? c.shared_inter : 0;

@@ -885,10 +885,7 @@ KernelPick pick_init(const InitArgs& a) {
     return {MOE_FN(init_lists_kernel), dim3((a.B + 63) / 64), dim3(64), 0};
 }
 
-int front_router_blocks(const RouterArgs& a, bool small_router) {
-    return small_router ? (a.E + 3) / 4
-                        : ((a.E + kRouterRowsPerMfmaTile - 1) / kRouterRowsPerMfmaTile) * a.ksplit;
-}
+int front_router_blocks(const RouterArgs& a) { return (a.E + 3) / 4; }
 
 // shared_tb: 0 when the shared expert runs on MFMA tiles, else its GEMV token count.
 KernelPick pick_front(const FrontArgs& f, bool small_router, bool select_in_router, int shared_tb) {
