@@ -153,6 +153,7 @@ struct FrontArgs {
     // partials [dks][B][2 Is] to `spart`
     float* spart;
     int32_t dks, dsteps;
+    int32_t dks_r, dsteps_r;  // the router tiles' K splits and steps (fewer partials for the top-k launch)
 };
 
 // Top-k launch (batch > 4): workgroups [0, sel_blocks) select and bucket

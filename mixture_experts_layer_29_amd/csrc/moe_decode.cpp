@@ -90,6 +90,7 @@ struct moe_decode_plan_s {
     int max_act;          // min(E, B*k)
     int ksplit, kslice;
     int dks, dsteps;      // dense front (batch > 4): K splits and 32-wide steps per split
+    int dks_r, dsteps_r;  // the same for its router tiles
     bool small_router;    // batch <= 4: one router launch; else MFMA router + top-k launch
     bool shared_stream;   // shared gate/up on the second stream instead of the front launch
     bool select_in_router;// batch <= 4: top-k + bucketing in the router's last workgroup
@@ -238,7 +239,7 @@ void fill_static_args(moe_decode_plan_s* p) {
     r.bias = c.router_bias;
     r.z = at<float>(p, p->L.z);
     r.zacc = at<float>(p, p->L.zacc);
-    r.nzpart = p->small_router ? 1 : p->dks;
+    r.nzpart = p->small_router ? 1 : p->dks_r;
     r.topk_idx = at<int32_t>(p, p->L.topk_idx);
     r.topk_w = at<float>(p, p->L.topk_w);
     r.meta = at<int32_t>(p, p->L.meta);
@@ -304,7 +305,7 @@ void fill_static_args(moe_decode_plan_s* p) {
     // workgroups, else in the front, one pair per workgroup.
     p->fa.router_blocks = p->select_in_gateup ? c.n_experts
                           : p->small_router     ? front_router_blocks(r)
-                                                : ((c.n_experts + 15) / 16) * p->dks;
+                                                : ((c.n_experts + 15) / 16) * p->dks_r;
     const bool sh_sel = p->shared_in_gateup;
     p->sga.shared_pairs = sh_sel ? c.shared_inter : 0;
     p->fa.shared_blocks = !shared_in_front(p) || sh_sel ? 0
@@ -313,6 +314,8 @@ void fill_static_args(moe_decode_plan_s* p) {
                                                 : (2 * c.shared_inter / 16) * p->dks;
     p->fa.dks = p->dks;
     p->fa.dsteps = p->dsteps;
+    p->fa.dks_r = p->dks_r;
+    p->fa.dsteps_r = p->dsteps_r;
     p->fa.spart = p->L.spart ? at<float>(p, p->L.spart) : nullptr;
     p->ta.spart = p->fa.spart;
     p->ta.hs = at<float>(p, p->L.hs);
@@ -674,6 +677,14 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
                 if (steps % s == 0) d = s;
         p->dks = d;
         p->dsteps = steps / d;
+        // router tiles: the fewest splits that leave at most 32 steps (two
+        // load rounds), so the top-k launch sums at most 8 partials in one round
+        int dr = 0;
+        for (int s = 1; s <= 32 && !dr; ++s)
+            if (steps % s == 0 && steps / s <= 32) dr = s;
+        if (!dr) dr = d;
+        p->dks_r = dr;
+        p->dsteps_r = steps / dr;
     }
     // single launch: batch <= 4, activations and every h row fit the LDS budget,
     // a down shape with an instantiation (I = 64, 128, 256 or 512..2048)
@@ -732,7 +743,7 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
                           c.shared_inter <= p->max_act * (c.inter / kPairsPerGemvTile);
     p->expert_major = c.batch > kDownOsMaxBatch;
     p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K, p->fused, p->expert_major,
-                       p->small_router ? 1 : p->dks,
+                       p->small_router ? 1 : p->dks_r,
                        !p->small_router && c.shared_inter > 0 && !p->shared_stream ? p->dks : 0);
     *out_plan = p;
     return MOE_OK;

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void front_dense_kernel(FrontArgs f) {
     const RouterArgs& a = f.r;
     const int b = blockIdx.x;
     if (b < f.router_blocks) {
-        dense_splitk_tile<NT>(a.wr, a.E, a.x, a.B, a.H, f.dsteps, b / f.dks, b % f.dks, a.zacc, s_red);
+        dense_splitk_tile<NT>(a.wr, a.E, a.x, a.B, a.H, f.dsteps_r, b / f.dks_r, b % f.dks_r, a.zacc, s_red);
     } else {
         const int l = b - f.router_blocks;
         dense_splitk_tile<NT>(f.s.w, 2 * f.s.n, a.x, a.B, a.H, f.dsteps, l / f.dks, l % f.dks, f.spart, s_red);
