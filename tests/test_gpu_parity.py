@@ -221,9 +221,11 @@ def test_tp8_zipf_skew(tp8_zipf):
     assert st.n_unique < 200
 
 
-@pytest.mark.parametrize("B,single,topk_launch", [(4, 0, 0), (4, 0, 1), (4, 2, 0), (16, 0, 0)])
+@pytest.mark.parametrize("B,single,topk_launch", [(4, 0, 0), (4, 0, 1), (4, 2, 0), (16, 0, 0), (64, 0, 0)])
 def test_tp8_identical_tokens_route_together(tp8, B, single, topk_launch):
-    """Every token identical: the k selected experts each get all B tokens.
+    """Every token identical: the k selected experts each get all B tokens
+    (B = 64: the gate/up MFMA tiles stage 64 tokens' activations and the down
+    tiles 64 h rows, 64 KiB, their largest).
     At B = 4 the default staged form runs them on GEMV tiles of 4 tokens; with
     the selection in the router (topk_launch 1) or inside the single launch,
     given an MFMA threshold of 4 tokens, and at B = 16 (default threshold) they
