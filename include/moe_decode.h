@@ -42,7 +42,9 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID = 1,      /* bad argument: NULL, out of range, misaligned, aliasing   */
-    MOE_ERR_UNSUPPORTED = 2,  /* valid layer the kernels do not cover; use another path   */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid layer the kernels do not cover; use another path
+                                 (the isolation rule of the Kimi K3 decode article,
+                                 Part 2 section 1: the caller falls back to its own path) */
     MOE_ERR_HIP = 3,          /* a HIP runtime call failed; message holds hipGetErrorString */
     MOE_ERR_NOMEM = 4,        /* host or device allocation failed                          */
     MOE_ERR_STATE = 5         /* call not valid in the plan's current state                */
@@ -50,13 +52,17 @@ typedef enum {
 
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
 
-/* Kernel family for the gate/up projection.
+/* Kernel family for the gate/up projection (the Kimi K3 decode article, Part 1
+ * section 1: small-matrix kernels at batch 1-2, split-K kernels at larger
+ * batches, which spread one matrix product over more GPU workers).
  *  SMALL_M: every expert is a full-K GEMV tile (lanes stream weight rows,
  *           fp32 dot products); the form for batch 1-2.
  *  SPLIT_K: experts with at least `mfma_min_tokens` tokens use split-K MFMA
  *           tiles (fp32 partials, last-arriving tile applies SiLU*up), the
  *           others GEMV tiles; the form for larger batches.
- *  AUTO:    SMALL_M for batch <= 2, SPLIT_K otherwise.                      */
+ *  AUTO:    SMALL_M for batch <= 2, SPLIT_K otherwise, and SPLIT_K also where
+ *           a GEMV tile's staged activations (2 * batch * hidden bytes) exceed
+ *           its LDS budget (60 KiB).                                        */
 typedef enum { MOE_VARIANT_AUTO = 0, MOE_VARIANT_SMALL_M = 1, MOE_VARIANT_SPLIT_K = 2 } moe_variant;
 
 typedef struct moe_decode_config {
@@ -75,7 +81,10 @@ typedef struct moe_decode_config {
     int32_t mfma_min_tokens; /* SPLIT_K: token count from which an expert uses MFMA
                                 tiles; 0 = library default (5, or less where the
                                 GEMV tiles' activation staging does not fit)         */
-    int32_t shared_stream;   /* 0: the shared expert's gate/up runs in trailing
+    int32_t shared_stream;   /* (the Kimi K3 decode article, Part 1 section 3: the
+                                shared expert on a stream of its own, overlapped
+                                with routing)
+                                0: the shared expert's gate/up runs in trailing
                                 workgroups of the router launch (overlap without a
                                 second queue); 1: on the plan's second stream,
                                 forked before the router and joined before the down
@@ -142,10 +151,22 @@ typedef struct moe_decode_stats {
 
 /* Validates `cfg` and builds a plan on the host.  Creates no device state, so
  * it works (and its errors can be tested) without a GPU.  router_bias is only
- * stored, not dereferenced.  *out_plan is set to NULL on failure. */
+ * stored, not dereferenced.  *out_plan is set to NULL on failure.
+ * Source: the Kimi K3 decode article, Part 1 section 1 (kernel shapes chosen
+ * per workload: small-matrix kernels at batch 1-2, split-K above), which is
+ * the choice the plan resolves (variant, mfma_min_tokens); and Part 2 section 1
+ * (isolate the changes): a shape the kernels do not cover is refused here with
+ * MOE_ERR_UNSUPPORTED, so the caller keeps its own path for it, and the choice
+ * made is readable through moe_decode_plan_info. */
 moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_plan);
 
 /* Runs the layer asynchronously on `stream`.
+ * Source: the Kimi K3 decode article, Part 1 sections 1 (small-matrix and
+ * split-K kernels by batch), 3 (router scores, tensor-parallel experts, the
+ * shared expert overlapped with routing) and 4 (small-batch decode is bound by
+ * loading weights); the Hungarian summary, section "Kevesebb kernel" (fewer
+ * kernels per layer); the article's "What's next" (per-step host work replayed
+ * as a graph).  The formulas are those at the top of this file.
  *   x        bf16 [B][H]                     layer input (and residual)
  *   router_w bf16 [E][H]                     router weight, one row per expert
  *   expert_w bf16 [E][2I][H] then [E][H][I]  per expert: W13 (rows 0..I-1 gate
@@ -168,7 +189,10 @@ moe_status moe_decode_forward(moe_decode_plan_t plan, const void* x, const void*
                               const void* expert_w, const void* shared_w, void* out,
                               void* stream);
 
-/* Enqueues on `stream` device-to-device copies of the last forward's routing:
+/* Source: the Kimi K3 decode article, Part 2 section 1 (a reviewer can trace
+ * what the optimised path selected) and Part 2 section 4 (expert selection
+ * decides which weights a step reads, so measurements report it).
+ * Enqueues on `stream` device-to-device copies of the last forward's routing:
  * topk_idx int32 [B][k] (expert ids, descending logit, ties to the lower id),
  * topk_w fp32 [B][k] (routing weights in the same order), n_unique int32 [1],
  * logits fp32 [B][E] (router logits including the bias).  Any destination may
@@ -176,14 +200,24 @@ moe_status moe_decode_forward(moe_decode_plan_t plan, const void* x, const void*
 moe_status moe_decode_routing(moe_decode_plan_t plan, int32_t* topk_idx, float* topk_w,
                               int32_t* n_unique, float* logits, void* stream);
 
-/* Synchronises the plan's streams and copies the device-side counters of the
- * last forward to *stats (host memory).  MOE_ERR_STATE before the first forward. */
+/* Source: the Kimi K3 decode article, Part 2 sections 1 (traceable selection)
+ * and 3 (tests must show that the changed path ran: the tile counters say
+ * which gate/up form each expert took).
+ * Waits for the stream of the plan's last forward (and the plan's second
+ * stream) to finish, then copies the device-side counters of that forward to
+ * *stats (host memory).  It synchronises nothing else.  MOE_ERR_STATE before
+ * the first forward. */
 moe_status moe_decode_read_stats(moe_decode_plan_t plan, moe_decode_stats* stats);
 
-/* Resolved plan properties (host memory). */
+/* Resolved plan properties (host memory): which launch form, kernel count and
+ * gate/up variant the plan runs.  Source: the Kimi K3 decode article, Part 2
+ * section 1 (it must be traceable when the optimised path is selected and how
+ * execution falls back; here the fallback is MOE_ERR_UNSUPPORTED at plan time). */
 moe_status moe_decode_plan_info(moe_decode_plan_t plan, moe_decode_info* info);
 
-/* Kernel timing.  While enabled, forward launches eagerly (no graph) and
+/* Kernel timing.  Source: the Kimi K3 decode article, Part 2 section 4
+ * (verify performance broadly, with reproducible results).
+ * While enabled, forward launches eagerly (no graph) and
  * records a HIP event pair around every kernel on the stream that kernel is
  * launched on.  moe_decode_profile_read synchronises those streams and writes,
  * per kernel slot, the summed milliseconds and the launch count over all
@@ -194,10 +228,13 @@ moe_status moe_decode_set_profiling(moe_decode_plan_t plan, int32_t enable);
 moe_status moe_decode_profile_read(moe_decode_plan_t plan, int32_t cap, double* total_ms,
                                    int32_t* launches, const char** names, int32_t* n);
 
-/* Frees the plan and everything it owns (waits for its streams).  NULL is a no-op. */
+/* Frees the plan and everything it owns (waits for the device).  NULL is a
+ * no-op.  (Plumbing: no passage of the pages defines it.) */
 moe_status moe_decode_destroy(moe_decode_plan_t plan);
 
-/* Message for the calling thread's last failed call ("" if none). */
+/* Message for the calling thread's last failed call ("" if none).  Source: the
+ * Kimi K3 decode article, Part 2 section 1 (a fallback to the standard path
+ * must be traceable: the message says why a shape was refused). */
 const char* moe_decode_last_error(void);
 
 #ifdef __cplusplus

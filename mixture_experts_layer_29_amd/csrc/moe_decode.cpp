@@ -129,6 +129,7 @@ struct moe_decode_plan_s {
     const void* args_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // in the arg blocks
     const void* graph_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};  // in the graph exec
     bool have_forward = false;
+    hipStream_t last_stream = nullptr;  // the stream of the last forward
 
     // profiling
     bool profiling = false;
@@ -431,6 +432,19 @@ void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, con
     }
 }
 
+// Frees what device_init created (any subset of it).
+void release_device_state(moe_decode_plan_s* p) {
+    if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
+    if (p->ev_join) (void)hipEventDestroy(p->ev_join);
+    if (p->s2) (void)hipStreamDestroy(p->s2);
+    if (p->ws) (void)hipFree(p->ws);
+    p->ev_fork = p->ev_join = nullptr;
+    p->s2 = nullptr;
+    p->ws = nullptr;
+}
+
+moe_status device_init_once(moe_decode_plan_s* p, hipStream_t stream, int dev);
+
 moe_status device_init(moe_decode_plan_s* p, hipStream_t stream) {
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
@@ -439,6 +453,16 @@ moe_status device_init(moe_decode_plan_s* p, hipStream_t stream) {
             return fail(MOE_ERR_STATE, "plan was set up on device %d, current device is %d", p->device, dev);
         return MOE_OK;
     }
+    const moe_status st = device_init_once(p, stream, dev);
+    if (st != MOE_OK) {
+        // leave nothing behind: a later forward starts from scratch
+        (void)hipStreamSynchronize(stream);
+        release_device_state(p);
+    }
+    return st;
+}
+
+moe_status device_init_once(moe_decode_plan_s* p, hipStream_t stream, int dev) {
     hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->ws), p->L.total);
     if (e != hipSuccess) {
         p->ws = nullptr;
@@ -635,10 +659,12 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
     if (!p) return fail(MOE_ERR_NOMEM, "host allocation of the plan failed");
     p->cfg = *cfg;
     const moe_decode_config& c = p->cfg;
-    p->variant = c.force_variant != MOE_VARIANT_AUTO ? c.force_variant
-                 : (c.batch <= 2 ? MOE_VARIANT_SMALL_M : MOE_VARIANT_SPLIT_K);
     // a GEMV tile stages its tokens' activations in LDS: at most this many tokens
     const int gemv_cap = (int)(kGemvLdsBytes / ((size_t)2 * c.hidden));
+    // AUTO: small-matrix tiles at batch <= 2 where their activations fit the
+    // LDS budget, split-K otherwise
+    p->variant = c.force_variant != MOE_VARIANT_AUTO ? c.force_variant
+                 : (c.batch <= 2 && c.batch <= gemv_cap ? MOE_VARIANT_SMALL_M : MOE_VARIANT_SPLIT_K);
     if (p->variant == MOE_VARIANT_SPLIT_K) {
         p->mfma_min = c.mfma_min_tokens ? c.mfma_min_tokens : kDefaultMfmaMin;
         if (p->mfma_min > kMaxBatch + 1) p->mfma_min = kMaxBatch + 1;
@@ -776,6 +802,7 @@ moe_status moe_decode_forward(moe_decode_plan_t p, const void* x, const void* ro
         std::memcpy(p->args_for, tuple, sizeof tuple);
     }
     p->have_forward = true;
+    p->last_stream = stream;
 
     if (cap == hipStreamCaptureStatusActive) return enqueue_eager(p, stream, nullptr);  // into the caller's graph
     if (p->profiling) {
@@ -826,7 +853,12 @@ moe_status moe_decode_read_stats(moe_decode_plan_t p, moe_decode_stats* stats) {
     g_err.clear();
     if (!p || !stats) return fail(MOE_ERR_INVALID, "NULL argument");
     if (!p->have_forward) return fail(MOE_ERR_STATE, "no forward has run on this plan");
-    HIP_TRY(hipDeviceSynchronize());
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(p->last_stream, &cap));
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(MOE_ERR_STATE, "the last forward's stream is being captured; read the stats after replay");
+    HIP_TRY(hipStreamSynchronize(p->last_stream));
+    if (p->s2) HIP_TRY(hipStreamSynchronize(p->s2));
     int32_t meta[M_COUNT];
     HIP_TRY(hipMemcpy(meta, p->ws + p->L.meta, sizeof meta, hipMemcpyDeviceToHost));
     stats->n_unique = meta[M_NACT];
@@ -910,10 +942,7 @@ moe_status moe_decode_destroy(moe_decode_plan_t p) {
         for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
         if (p->exec) (void)hipGraphExecDestroy(p->exec);
         if (p->graph) (void)hipGraphDestroy(p->graph);
-        if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
-        if (p->ev_join) (void)hipEventDestroy(p->ev_join);
-        if (p->s2) (void)hipStreamDestroy(p->s2);
-        if (p->ws) (void)hipFree(p->ws);
+        release_device_state(p);
     }
     delete p;
     return st;

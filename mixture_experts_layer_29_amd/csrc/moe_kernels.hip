@@ -3,12 +3,16 @@
 // is in moe_layer.h).
 //
 // One layer is, on the main stream:
-//   front      batch <= 4: front_small -- router GEMV, then the last workgroup
+//   front      batch 1: front_split -- one router row per workgroup, logits to
+//              z; the routed gate/up launch then selects in every workgroup
+//              (gateup_select);
+//              batch 2-4: front_small -- router GEMV, then the last workgroup
 //              to arrive selects the top-k experts of every token, computes the
 //              routing weights and buckets the (token, slot) pairs by expert;
-//              batch > 4: front_mfma -- split-K MFMA router GEMM accumulating
-//              fp32 logits -- then topk_bucket -- one wave per token selects
-//              the top-k, the last workgroup buckets with an LDS histogram;
+//              batch > 4: front_dense -- dense split-K MFMA tiles writing plain
+//              fp32 partial logits (no atomics) -- then topk_bucket -- which
+//              sums the partials in a fixed order, selects with one wave per
+//              token, and buckets with an LDS histogram in its last workgroup;
 //              trailing workgroups of the front launch run the shared expert's
 //              gate/up, which needs only x;
 //   gateup     grouped gate/up projection + SiLU*up over the active experts:

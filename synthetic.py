@@ -142,6 +142,19 @@ def _dev_normal(n: int, std: float, gen: torch.Generator, device) -> torch.Tenso
     return torch.randn(n, generator=gen, device=device, dtype=torch.float32).mul_(std).to(torch.bfloat16)
 
 
+def _dev_base(wl: Workload, layer: int) -> int:
+    return (wl.seed * 1000 + layer * 16) * 1000
+
+
+def device_router(wl: Workload, device="cuda", layer: int = 0) -> torch.Tensor:
+    """The router weight [E x H] of ``device_layer(wl, device, layer)`` alone
+    (bf16, N(0, wl.router_std)); workloads that differ only in router_std draw
+    the same normal variates, scaled differently."""
+    g = torch.Generator(device=device)
+    g.manual_seed(_dev_base(wl, layer) + T_WR)
+    return _dev_normal(wl.n_experts * wl.hidden, wl.router_std, g, device).view(wl.n_experts, wl.hidden)
+
+
 def device_layer(wl: Workload, device="cuda", layer: int = 0) -> dict:
     """Weights drawn on the device in the GPU library's packed layout.
 
@@ -149,10 +162,9 @@ def device_layer(wl: Workload, device="cuda", layer: int = 0) -> dict:
     router_w = [E x H]; all bf16.  ``layer`` selects an independent draw.
     """
     E, H, I, Is = wl.n_experts, wl.hidden, wl.inter, wl.shared_inter
-    base = (wl.seed * 1000 + layer * 16) * 1000
+    base = _dev_base(wl, layer)
     g = torch.Generator(device=device)
-    g.manual_seed(base + T_WR)
-    wr = _dev_normal(E * H, wl.router_std, g, device).view(E, H)
+    wr = device_router(wl, device, layer)
     expert_w = torch.empty(E * 3 * I * H, dtype=torch.bfloat16, device=device)
     n13 = 2 * I * H
     for e in range(E):

@@ -55,6 +55,12 @@ class DeviceLayer:
         self._cache13, self._cache2 = {}, {}
         self._s = None
 
+    def clear_cache(self):
+        """Drops the host copies of expert weights (bounds host memory when a
+        test walks many experts of a large layer)."""
+        self._cache13.clear()
+        self._cache2.clear()
+
     def expert_bits(self, e: int):
         wl = self.wl
         E, H, I = wl.n_experts, wl.hidden, wl.inter

@@ -49,6 +49,9 @@ def plan_status(c):
     dict(inter=64, shared_inter=64), dict(inter=512, shared_inter=1024), dict(top_k=16),
     dict(n_experts=1024), dict(n_experts=1, top_k=1), dict(hidden=64, n_experts=3, top_k=3, inter=64,
                                                           shared_inter=0),
+    dict(hidden=16384, batch=1), dict(hidden=16384, batch=2), dict(hidden=16384, batch=64, n_experts=1024,
+                                                                   top_k=16),
+    dict(n_experts=8, top_k=8), dict(n_experts=16, top_k=16),
 ])
 def test_supported_configs_plan(kw):
     assert plan_status(cfg(**kw)) == moe.MOE_OK
@@ -214,6 +217,15 @@ def test_topk_launch_policy(batch):
     assert i.topk_launch == default_tl and i.shared_mfma == 0
     i = info(single_launch=moe.SINGLE_REQUIRED)
     assert i.topk_launch == 0 and i.n_kernels == 1
+
+
+@pytest.mark.parametrize("batch,variant", [(1, moe.VARIANT_SMALL_M), (2, moe.VARIANT_SPLIT_K)])
+def test_auto_variant_falls_back_where_gemv_staging_does_not_fit(batch, variant):
+    """At hidden 16384 a GEMV tile's LDS holds one token's activations: AUTO
+    takes split-K tiles from batch 2 instead of refusing the shape."""
+    p = moe.Plan(cfg(hidden=16384, batch=batch))
+    assert p.info().variant == variant
+    p.destroy()
 
 
 def test_forced_variant_and_threshold():

@@ -333,10 +333,35 @@ def full():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("batch,sample", [(1, None), (16, [0, 7, 15]), (32, [0, 13, 31]),
-                                          (64, [0, 21, 42, 63])])
-def test_unsharded_sampled(full, batch, sample):
-    check(full, shape_of(synthetic.FULL), batch, "unsharded B=%d" % batch, sample=sample)
+def check_chunked(layer, shape, batch, label, chunk=8, offset=0, **plan_kw):
+    """Every token compared with the oracle, `chunk` tokens at a time (the
+    host copies of the experts a chunk touches are dropped after it, so host
+    memory stays bounded on large layers); n_unique against the oracle's
+    selection of the whole batch."""
+    x, _ = gap_x(layer, shape, batch, offset)
+    plan = make_plan(layer, shape, batch, **plan_kw)
+    out, idx, w, nu = run_gpu(plan, layer, x, shape)
+    z = oracle.router_logits(shape, x, layer.wr_bits, layer.bias_np)
+    idx_all, _ = oracle.select(shape, z)
+    assert nu == len(np.unique(idx_all)), "n_unique %d vs oracle %d" % (nu, len(np.unique(idx_all)))
+    for c0 in range(0, batch, chunk):
+        rows = np.arange(c0, min(batch, c0 + chunk))
+        out64, idx_o, w_o = run_oracle(layer, shape, x[rows])
+        compare(out[torch.from_numpy(rows).cuda()], idx[rows], w[rows], out64, idx_o, w_o,
+                "%s tokens %d-%d" % (label, rows[0], rows[-1]))
+        layer.clear_cache()
+    st = plan.stats()
+    assert st.error_flags == 0 and st.n_unique == nu
+    info = plan.info()
+    plan.destroy()
+    return st, info
+
+
+@pytest.mark.parametrize("batch", [1, 16, 32, 64])
+def test_unsharded_every_token(full, batch):
+    st, info = check_chunked(full, shape_of(synthetic.FULL), batch, "unsharded B=%d" % batch)
+    if batch > 4:  # expert-major down with MFMA tiles for the shared expert's column blocks
+        assert info.shared_mfma == 1
 
 
 # --------------------------------------------------------------- edge shapes
@@ -354,6 +379,11 @@ EDGE = [
     ("experts1024", 256, 1024, 8, 64, 0, 1, 1, 1.0, True, 20),
     ("scaled_softmax_unnormalised", 256, 16, 4, 128, 128, 0, 0, 2.5, False, 12),
     ("sigmoid_unnormalised", 256, 16, 4, 128, 128, 1, 0, 1.0, True, 12),
+    # k = E: every expert is selected for every token
+    ("topk_equals_experts_softmax", 256, 8, 8, 128, 128, 0, 1, 1.0, False, 6),
+    ("topk_equals_experts_sigmoid", 512, 16, 16, 64, 64, 1, 1, 1.0, True, 5),
+    # the largest hidden size, expert count, top-k and batch the library takes
+    ("max_dims", 16384, 1024, 16, 64, 64, 1, 1, 1.0, True, 64),
 ]
 
 
@@ -362,7 +392,7 @@ def test_edge_shapes(case):
     name, H, E, k, I, Is, score, ren, scale, bias, B = case
     wl = synthetic.Workload(name, H, E, k, I, Is, B, score, router_std=0.05, weight_std=0.05,
                             zipf_s=1.1 if bias else None, seed=3)
-    layer = DeviceLayer(wl, host=True)
+    layer = DeviceLayer(wl, host=E * 3 * I * H <= (64 << 20))
     shape = shape_of(wl, renormalize=ren, routed_scale=scale)
     for b in sorted({1, B}):
         check(layer, shape, b, "%s B=%d" % (name, b))
