@@ -189,6 +189,28 @@ moe_status moe_decode_forward(moe_decode_plan_t plan, const void* x, const void*
                               const void* expert_w, const void* shared_w, void* out,
                               void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * layer as moe_decode_forward on the same kernels, launched directly on
+ * `stream` (no graph, no second stream, no events), with every scratch buffer
+ * (counters, logits, routing, work lists, h, split-K and down partials) in a
+ * static device array of the library, one copy per GPU, at most 48 MiB; the
+ * plan's own workspace is neither allocated nor used.  Calls no hipMalloc,
+ * hipFree or other allocating routine.  Arguments, layout and ownership as for
+ * moe_decode_forward.  Each call first clears what must start at zero and
+ * writes the shared expert's work list in the array (one small extra launch).
+ * Errors: MOE_ERR_UNSUPPORTED when the plan's workspace exceeds the array
+ * (moe_decode_plan_info reports workspace_bytes), or when the plan asks for
+ * the single launch (single_launch = 2) or a second stream (shared_stream =
+ * 1); MOE_ERR_INVALID as for moe_decode_forward.  Every call on a GPU, from
+ * any plan, shares that GPU's array and it keeps the last call's contents:
+ * calls that overlap on one GPU (concurrent streams, threads) race and must
+ * not be issued; moe_decode_routing and moe_decode_read_stats after this call
+ * read the array, so no other call may run on that GPU between them. */
+moe_status moe_decode_forward_noalloc(moe_decode_plan_t plan, const void* x, const void* router_w,
+                                      const void* expert_w, const void* shared_w, void* out,
+                                      void* stream);
+
 /* Source: the Kimi K3 decode article, Part 2 section 1 (a reviewer can trace
  * what the optimised path selected) and Part 2 section 4 (expert selection
  * decides which weights a step reads, so measurements report it).

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_decode.so")
 HEADER = os.path.join(_ROOT, "include", "moe_decode.h")
 _CSRC = os.path.join(_HERE, "csrc")
 SOURCES = [os.path.join(_CSRC, f) for f in ("moe_kernels.hip", "moe_layer_tb1.hip", "moe_layer_tb2.hip",
-                                             "moe_layer_tb4.hip", "moe_decode.cpp")]
+                                             "moe_layer_tb4.hip", "moe_scratch.hip", "moe_decode.cpp")]
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_NOMEM, MOE_ERR_STATE = range(6)
 STATUS_NAMES = ["MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP", "MOE_ERR_NOMEM",
@@ -28,7 +28,8 @@ VARIANT_AUTO, VARIANT_SMALL_M, VARIANT_SPLIT_K = 0, 1, 2
 VARIANT_NAMES = {0: "AUTO", 1: "SMALL_M", 2: "SPLIT_K"}
 SINGLE_AUTO, SINGLE_OFF, SINGLE_REQUIRED = 0, 1, 2
 
-EXPORTS = ["moe_decode_plan", "moe_decode_forward", "moe_decode_routing", "moe_decode_read_stats",
+EXPORTS = ["moe_decode_plan", "moe_decode_forward", "moe_decode_forward_noalloc", "moe_decode_routing",
+           "moe_decode_read_stats",
            "moe_decode_plan_info", "moe_decode_set_profiling", "moe_decode_profile_read",
            "moe_decode_destroy", "moe_decode_last_error"]
 
@@ -101,6 +102,7 @@ def lib() -> ctypes.CDLL:
         P = ctypes.c_void_p
         L.moe_decode_plan.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(P)]
         L.moe_decode_forward.argtypes = [P, P, P, P, P, P, P]
+        L.moe_decode_forward_noalloc.argtypes = [P, P, P, P, P, P, P]
         L.moe_decode_routing.argtypes = [P, P, P, P, P, P]
         L.moe_decode_read_stats.argtypes = [P, ctypes.POINTER(Stats)]
         L.moe_decode_plan_info.argtypes = [P, ctypes.POINTER(Info)]
@@ -164,6 +166,11 @@ class Plan:
     def forward(self, x, router_w, expert_w, shared_w, out, stream=None):
         _check(lib().moe_decode_forward(self.handle, _ptr(x), _ptr(router_w), _ptr(expert_w),
                                         _ptr(shared_w), _ptr(out), _stream(stream)))
+        return out
+
+    def forward_noalloc(self, x, router_w, expert_w, shared_w, out, stream=None):
+        _check(lib().moe_decode_forward_noalloc(self.handle, _ptr(x), _ptr(router_w), _ptr(expert_w),
+                                                _ptr(shared_w), _ptr(out), _stream(stream)))
         return out
 
     def routing(self, topk_idx=None, topk_w=None, n_unique=None, logits=None, stream=None):

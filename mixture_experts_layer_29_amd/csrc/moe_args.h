@@ -198,13 +198,19 @@ struct LayerArgs {
     int32_t shared_mfma;    // shared expert on MFMA tiles
 };
 
-// Writes the shared expert's constant work list (run once per workspace).
+// Writes the shared expert's constant work list (once per workspace, or before
+// every allocation-free forward); with zero_meta it also clears the meta block
+// and the words [zero, zero + zero_words) -- the split-K partials and tile
+// counters, which must start at zero -- with plain stores (no memset node).
 struct InitArgs {
     int32_t* meta;
     int32_t* sh_act_e;   // [1]
     int32_t* sh_act_off; // [2]
     int32_t* sh_perm;    // [B]
     int32_t B;
+    int32_t zero_meta;
+    uint32_t* zero;      // 16-byte aligned, or null
+    long long zero_words;// a multiple of 4
 };
 
 // A kernel and its launch shape, chosen for one argument block.
@@ -216,6 +222,12 @@ struct KernelPick {
 };
 
 KernelPick pick_init(const InitArgs& a);
+
+// Device scratch of the allocation-free forward: a static array, one copy per
+// GPU, held until the process ends (moe_scratch.hip).
+constexpr size_t kScratchBytes = 48u << 20;
+// The current device's copy (its device address, looked up once per device).
+hipError_t scratch_for_current_device(void** ptr, size_t* bytes);
 // Front launch: batch <= 4 (router GEMV, with top-k + bucketing in the last
 // workgroup when select_in_router) or larger (router MFMA).  Otherwise top-k
 // and bucketing follow in pick_topk's launch.  shared_tb: 0 when the shared

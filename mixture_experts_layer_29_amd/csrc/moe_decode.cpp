@@ -74,9 +74,24 @@ const char* kSlotNames[S_COUNT] = {"front", "topk_bucket", "gateup_routed", "gat
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Argument blocks and kernel picks of one forward; the pointer fields are
+// refreshed when the caller's pointers change.
+struct Launches {
+    FrontArgs fa{};
+    GateUpArgs ga{};
+    TopkArgs ta{};        // top-k launch (router part refreshed per forward)
+    SelGateUpArgs sga{};  // gate/up launch of the select-in-gate/up form
+    DownArgs da{};        // down of the single launch / output-stationary down
+    DownXArgs dx{};       // expert-major down of the staged launches
+    LayerArgs la{};
+    InitArgs ia{};        // per-call set-up of the allocation-free forward
+    KernelPick kf{}, kt{}, kg{}, ks{}, kd{}, kl{}, kc{}, ki{};
+};
+
 struct Layout {
     size_t meta, z, zacc, topk_idx, topk_w, act_e, act_off, perm, sh_act_e, sh_act_off, sh_perm;
     size_t h, hs, g_acc, g_acc_s, tile_cnt, tile_cnt_s, s_out, part, part_s, spart, total;
+    size_t zero_end;  // [g_acc, zero_end): split-K partials and tile counters, zero between uses
 };
 
 }  // namespace
@@ -109,17 +124,12 @@ struct moe_decode_plan_s {
     hipStream_t s2 = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
-    // argument blocks; the pointer fields are refreshed per forward
-    FrontArgs fa{};
-    RouterArgs& ra = fa.r;
-    GateUpArgs& gs = fa.s;
-    GateUpArgs ga{};
-    TopkArgs ta{};        // top-k launch (router part refreshed per forward)
-    SelGateUpArgs sga{};  // gate/up launch of the select-in-gate/up form
-    DownArgs da{};     // down of the single launch
-    DownXArgs dx{};    // down of the staged launches
-    LayerArgs la{};
-    KernelPick kf{}, kt{}, kg{}, ks{}, kd{}, kl{}, kc{};
+    // argument blocks over the plan's workspace (m) and over the device's
+    // static scratch array (na, the allocation-free forward)
+    Launches m{}, na{};
+    char* na_ws = nullptr;      // the scratch the na blocks point into
+    const void* na_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    const char* last_ws = nullptr;  // workspace of the last forward (routing / stats read it)
 
     // graph
     hipGraph_t graph = nullptr;
@@ -129,6 +139,7 @@ struct moe_decode_plan_s {
     const void* args_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // in the arg blocks
     const void* graph_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};  // in the graph exec
     bool have_forward = false;
+    bool m_valid = false;  // the m blocks hold the pointers in args_for
     hipStream_t last_stream = nullptr;  // the stream of the last forward
 
     // profiling
@@ -216,6 +227,9 @@ Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fus
         L.g_acc_s = take(B * 2 * (Is ? Is : 1) * 4);
         L.tile_cnt = take((size_t)max_act * (I / kPairsPerMfmaTile) * 4);
         L.tile_cnt_s = take((Is / kPairsPerMfmaTile + 1) * 4);
+        L.zero_end = o;
+    } else {
+        L.g_acc = L.zero_end = o;
     }
     if (fused && Is) L.s_out = take(B * c.hidden * 4);
     if (expert_major) {  // per-pair / per-shared-block partials of the expert-major down
@@ -228,25 +242,32 @@ Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fus
 }
 
 template <class T>
-T* at(moe_decode_plan_s* p, size_t off) {
-    return reinterpret_cast<T*>(p->ws + off);
+T* at(char* ws, size_t off) {
+    return reinterpret_cast<T*>(ws + off);
 }
 
-// Fills the argument blocks whose pointers do not depend on the caller.
-void fill_static_args(moe_decode_plan_s* p) {
+// Fills the argument blocks whose pointers do not depend on the caller, over
+// the workspace `ws` (laid out as p->L).  clear: the set-up launch also clears
+// the counters and split-K partials (a workspace another plan may have used).
+void fill_static_args(moe_decode_plan_s* p, char* ws, Launches& A, bool clear) {
     const moe_decode_config& c = p->cfg;
     const bool split = p->variant == MOE_VARIANT_SPLIT_K;
-    RouterArgs& r = p->ra;
+    A.ia = InitArgs{at<int32_t>(ws, p->L.meta), at<int32_t>(ws, p->L.sh_act_e), at<int32_t>(ws, p->L.sh_act_off),
+                    at<int32_t>(ws, p->L.sh_perm), c.batch, clear ? 1 : 0,
+                    clear ? at<uint32_t>(ws, p->L.g_acc) : nullptr,
+                    clear ? (long long)((p->L.zero_end - p->L.g_acc) / 4) : 0};
+    A.ki = pick_init(A.ia);
+    RouterArgs& r = A.fa.r;
     r.bias = c.router_bias;
-    r.z = at<float>(p, p->L.z);
-    r.zacc = at<float>(p, p->L.zacc);
+    r.z = at<float>(ws, p->L.z);
+    r.zacc = at<float>(ws, p->L.zacc);
     r.nzpart = p->small_router ? 1 : p->dks_r;
-    r.topk_idx = at<int32_t>(p, p->L.topk_idx);
-    r.topk_w = at<float>(p, p->L.topk_w);
-    r.meta = at<int32_t>(p, p->L.meta);
-    r.act_e = at<int32_t>(p, p->L.act_e);
-    r.act_off = at<int32_t>(p, p->L.act_off);
-    r.perm = at<int32_t>(p, p->L.perm);
+    r.topk_idx = at<int32_t>(ws, p->L.topk_idx);
+    r.topk_w = at<float>(ws, p->L.topk_w);
+    r.meta = at<int32_t>(ws, p->L.meta);
+    r.act_e = at<int32_t>(ws, p->L.act_e);
+    r.act_off = at<int32_t>(ws, p->L.act_off);
+    r.perm = at<int32_t>(ws, p->L.perm);
     r.H = c.hidden;
     r.E = c.n_experts;
     r.k = c.top_k;
@@ -258,16 +279,16 @@ void fill_static_args(moe_decode_plan_s* p) {
     r.tiles_per_expert = c.inter / kPairsPerGemvTile;
     r.mfma_tiles_per_expert = (c.inter / kPairsPerMfmaTile) * p->ksplit;
 
-    GateUpArgs& g = p->ga;
+    GateUpArgs& g = A.ga;
     g.expert_stride = 2LL * c.inter * c.hidden;
-    g.n_act = at<int32_t>(p, p->L.meta) + M_NACT;
+    g.n_act = at<int32_t>(ws, p->L.meta) + M_NACT;
     g.act_e = r.act_e;
     g.act_off = r.act_off;
     g.perm = r.perm;
     g.pair_div = c.top_k;
-    g.h = at<float>(p, p->L.h);
-    g.g_acc = split ? at<float>(p, p->L.g_acc) : nullptr;
-    g.tile_cnt = split ? at<uint32_t>(p, p->L.tile_cnt) : nullptr;
+    g.h = at<float>(ws, p->L.h);
+    g.g_acc = split ? at<float>(ws, p->L.g_acc) : nullptr;
+    g.tile_cnt = split ? at<uint32_t>(ws, p->L.tile_cnt) : nullptr;
     g.meta = r.meta;
     g.H = c.hidden;
     g.n = c.inter;
@@ -279,16 +300,16 @@ void fill_static_args(moe_decode_plan_s* p) {
     g.kslice = p->kslice;
 
     if (has_shared(p)) {
-        GateUpArgs& s = p->gs;
+        GateUpArgs& s = A.fa.s;
         s.expert_stride = 0;
-        s.n_act = at<int32_t>(p, p->L.meta) + M_SHARED_NACT;
-        s.act_e = at<int32_t>(p, p->L.sh_act_e);
-        s.act_off = at<int32_t>(p, p->L.sh_act_off);
-        s.perm = at<int32_t>(p, p->L.sh_perm);
+        s.n_act = at<int32_t>(ws, p->L.meta) + M_SHARED_NACT;
+        s.act_e = at<int32_t>(ws, p->L.sh_act_e);
+        s.act_off = at<int32_t>(ws, p->L.sh_act_off);
+        s.perm = at<int32_t>(ws, p->L.sh_perm);
         s.pair_div = 1;
-        s.h = at<float>(p, p->L.hs);
-        s.g_acc = split ? at<float>(p, p->L.g_acc_s) : nullptr;
-        s.tile_cnt = split ? at<uint32_t>(p, p->L.tile_cnt_s) : nullptr;
+        s.h = at<float>(ws, p->L.hs);
+        s.g_acc = split ? at<float>(ws, p->L.g_acc_s) : nullptr;
+        s.tile_cnt = split ? at<uint32_t>(ws, p->L.tile_cnt_s) : nullptr;
         s.meta = r.meta;
         s.H = c.hidden;
         s.n = c.shared_inter;
@@ -304,34 +325,34 @@ void fill_static_args(moe_decode_plan_s* p) {
     // workgroup; the shared expert's gate/up row pairs run in the gate/up
     // launch (one per workgroup, during the selection) when it has enough
     // workgroups, else in the front, one pair per workgroup.
-    p->fa.router_blocks = p->select_in_gateup ? c.n_experts
+    A.fa.router_blocks = p->select_in_gateup ? c.n_experts
                           : p->small_router     ? front_router_blocks(r)
                                                 : ((c.n_experts + 15) / 16) * p->dks_r;
     const bool sh_sel = p->shared_in_gateup;
-    p->sga.shared_pairs = sh_sel ? c.shared_inter : 0;
-    p->fa.shared_blocks = !shared_in_front(p) || sh_sel ? 0
+    A.sga.shared_pairs = sh_sel ? c.shared_inter : 0;
+    A.fa.shared_blocks = !shared_in_front(p) || sh_sel ? 0
                           : p->select_in_gateup ? c.shared_inter
                           : p->small_router     ? c.shared_inter / kPairsPerGemvTile
                                                 : (2 * c.shared_inter / 16) * p->dks;
-    p->fa.dks = p->dks;
-    p->fa.dsteps = p->dsteps;
-    p->fa.dks_r = p->dks_r;
-    p->fa.dsteps_r = p->dsteps_r;
-    p->fa.spart = p->L.spart ? at<float>(p, p->L.spart) : nullptr;
-    p->ta.spart = p->fa.spart;
-    p->ta.hs = at<float>(p, p->L.hs);
-    p->ta.Is = c.shared_inter;
-    p->ta.nspart = p->L.spart ? p->dks : 0;
-    p->ta.sel_blocks = (c.batch + 3) / 4;
+    A.fa.dks = p->dks;
+    A.fa.dsteps = p->dsteps;
+    A.fa.dks_r = p->dks_r;
+    A.fa.dsteps_r = p->dsteps_r;
+    A.fa.spart = p->L.spart ? at<float>(ws, p->L.spart) : nullptr;
+    A.ta.spart = A.fa.spart;
+    A.ta.hs = at<float>(ws, p->L.hs);
+    A.ta.Is = c.shared_inter;
+    A.ta.nspart = p->L.spart ? p->dks : 0;
+    A.ta.sel_blocks = (c.batch + 3) / 4;
 
-    DownArgs& d = p->da;
+    DownArgs& d = A.da;
     d.n_act = g.n_act;
     d.act_e = r.act_e;
     d.act_off = r.act_off;
     d.perm = r.perm;
     d.topk_w = r.topk_w;
     d.h = g.h;
-    d.hs = at<float>(p, p->L.hs);
+    d.hs = at<float>(ws, p->L.hs);
     d.H = c.hidden;
     d.I = c.inter;
     d.Is = c.shared_inter;
@@ -340,9 +361,9 @@ void fill_static_args(moe_decode_plan_s* p) {
     d.add_residual = c.add_residual;
     d.n_experts = c.n_experts;
     d.h_in_lds = down_h_lds_bytes(c.batch, c.top_k, c.inter, c.shared_inter) <= kDownHLds ? 1 : 0;
-    d.s_out = (p->fused && has_shared(p)) ? at<float>(p, p->L.s_out) : nullptr;
+    d.s_out = (p->fused && has_shared(p)) ? at<float>(ws, p->L.s_out) : nullptr;
 
-    DownXArgs& x = p->dx;
+    DownXArgs& x = A.dx;
     x.n_act = g.n_act;
     x.act_e = r.act_e;
     x.act_off = r.act_off;
@@ -350,8 +371,8 @@ void fill_static_args(moe_decode_plan_s* p) {
     x.topk_w = r.topk_w;
     x.h = g.h;
     x.hs = d.hs;
-    x.part = p->expert_major ? at<float>(p, p->L.part) : nullptr;
-    x.part_s = p->expert_major ? at<float>(p, p->L.part_s) : nullptr;
+    x.part = p->expert_major ? at<float>(ws, p->L.part) : nullptr;
+    x.part_s = p->expert_major ? at<float>(ws, p->L.part_s) : nullptr;
     x.meta = r.meta;
     x.H = c.hidden;
     x.I = c.inter;
@@ -365,7 +386,7 @@ void fill_static_args(moe_decode_plan_s* p) {
     x.mfma_min_tokens = p->mfma_min;
 
     if (p->fused) {
-        LayerArgs& l = p->la;
+        LayerArgs& l = A.la;
         const int R = down_rows_per_block(c.inter);
         l.n_router = (c.n_experts + 3) / 4;
         l.n_sgu = has_shared(p) ? c.shared_inter / kPairsPerGemvTile : 0;
@@ -381,54 +402,54 @@ void fill_static_args(moe_decode_plan_s* p) {
 
 int layer_tasks(const LayerArgs& l) { return l.n_router + l.n_sgu + l.n_sdown + l.n_gu + l.n_down; }
 
-void set_pointers(moe_decode_plan_s* p, const void* x, const void* router_w, const void* expert_w,
+void set_pointers(moe_decode_plan_s* p, Launches& A, const void* x, const void* router_w, const void* expert_w,
                   const void* shared_w, void* out) {
     const moe_decode_config& c = p->cfg;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const uint16_t* ew = static_cast<const uint16_t*>(expert_w);
     const uint16_t* sw = static_cast<const uint16_t*>(shared_w);
-    p->ra.x = xb;
-    p->ra.wr = static_cast<const uint16_t*>(router_w);
-    p->ga.x = xb;
-    p->ga.w = ew;
-    p->gs.x = xb;
-    p->gs.w = sw;
-    p->da.x = xb;
-    p->da.w2 = ew + (size_t)c.n_experts * 2 * c.inter * c.hidden;
-    p->da.s2 = has_shared(p) ? sw + (size_t)2 * c.shared_inter * c.hidden : nullptr;
-    p->da.out = static_cast<uint16_t*>(out);
-    p->dx.x = xb;
-    p->dx.w2 = p->da.w2;
-    p->dx.s2 = p->da.s2;
-    p->dx.out = p->da.out;
+    A.fa.r.x = xb;
+    A.fa.r.wr = static_cast<const uint16_t*>(router_w);
+    A.ga.x = xb;
+    A.ga.w = ew;
+    A.fa.s.x = xb;
+    A.fa.s.w = sw;
+    A.da.x = xb;
+    A.da.w2 = ew + (size_t)c.n_experts * 2 * c.inter * c.hidden;
+    A.da.s2 = has_shared(p) ? sw + (size_t)2 * c.shared_inter * c.hidden : nullptr;
+    A.da.out = static_cast<uint16_t*>(out);
+    A.dx.x = xb;
+    A.dx.w2 = A.da.w2;
+    A.dx.s2 = A.da.s2;
+    A.dx.out = A.da.out;
     if (p->select_in_gateup) {
-        p->sga.r = p->ra;
-        p->sga.g = p->ga;
-        p->sga.s = p->gs;
-        p->kf = pick_front_split(p->fa);
-        p->kg = pick_gateup_select(p->sga, p->max_act);
+        A.sga.r = A.fa.r;
+        A.sga.g = A.ga;
+        A.sga.s = A.fa.s;
+        A.kf = pick_front_split(A.fa);
+        A.kg = pick_gateup_select(A.sga, p->max_act);
     } else {
-        p->kf = pick_front(p->fa, p->small_router, p->select_in_router, p->shared_mfma ? 0 : c.batch);
+        A.kf = pick_front(A.fa, p->small_router, p->select_in_router, p->shared_mfma ? 0 : c.batch);
         if (topk_own_launch(p)) {
-            p->ta.r = p->ra;
-            p->kt = pick_topk(p->ta);
+            A.ta.r = A.fa.r;
+            A.kt = pick_topk(A.ta);
         }
-        p->kg = pick_gateup(p->ga, p->max_act, p->routed_gemv_tb);
+        A.kg = pick_gateup(A.ga, p->max_act, p->routed_gemv_tb);
     }
-    if (has_shared(p) && p->shared_stream) p->ks = pick_gateup(p->gs, 1, p->shared_mfma ? 1 : c.batch);
+    if (has_shared(p) && p->shared_stream) A.ks = pick_gateup(A.fa.s, 1, p->shared_mfma ? 1 : c.batch);
     if (p->expert_major) {
-        p->kd = pick_down_x(p->dx);
-        p->kc = pick_combine(p->dx);
+        A.kd = pick_down_x(A.dx);
+        A.kc = pick_combine(A.dx);
     } else {
-        p->kd = pick_down_os(p->da);
-        if (!p->kd.func) p->kd = pick_down(p->da);
+        A.kd = pick_down_os(A.da);
+        if (!A.kd.func) A.kd = pick_down(A.da);
     }
     if (p->fused) {
-        p->la.f = p->fa;
-        p->la.g = p->ga;
-        p->la.d = p->da;
-        p->kl = pick_layer(p->la, p->layer_lds);
-        p->kl.grid = dim3(p->layer_grid);
+        A.la.f = A.fa;
+        A.la.g = A.ga;
+        A.la.d = A.da;
+        A.kl = pick_layer(A.la, p->layer_lds);
+        A.kl.grid = dim3(p->layer_grid);
     }
 }
 
@@ -475,16 +496,16 @@ moe_status device_init_once(moe_decode_plan_s* p, hipStream_t stream, int dev) {
     HIP_TRY(hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming));
     // zero once: counters re-arm themselves and split-K partials are cleared after use
     HIP_TRY(hipMemsetAsync(p->ws, 0, p->L.total, stream));
-    fill_static_args(p);
-    InitArgs ia{at<int32_t>(p, p->L.meta), at<int32_t>(p, p->L.sh_act_e), at<int32_t>(p, p->L.sh_act_off),
-                at<int32_t>(p, p->L.sh_perm), p->cfg.batch};
-    KernelPick ki = pick_init(ia);
-    void* args[] = {&ia};
-    HIP_TRY(hipLaunchKernel(ki.func, ki.grid, ki.block, args, ki.lds, stream));
+    Launches& A = p->m;
+    fill_static_args(p, p->ws, A, false);
+    {
+        void* args[] = {&A.ia};
+        HIP_TRY(hipLaunchKernel(A.ki.func, A.ki.grid, A.ki.block, args, A.ki.lds, stream));
+    }
     if (p->fused) {
         // every workgroup of the single launch must be resident at once: the grid is
         // what the occupancy allows on this device, capped at the task count
-        const KernelPick k = pick_layer(p->la, p->layer_lds);
+        const KernelPick k = pick_layer(A.la, p->layer_lds);
         if (!k.func) return fail(MOE_ERR_UNSUPPORTED, "no single-launch kernel for this shape");
         if (p->layer_lds > 64 * 1024)
             HIP_TRY(hipFuncSetAttribute(k.func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p->layer_lds));
@@ -494,13 +515,13 @@ moe_status device_init_once(moe_decode_plan_s* p, hipStream_t stream, int dev) {
         if (per_cu < 1 || cus < 1)
             return fail(MOE_ERR_UNSUPPORTED, "single-launch kernel does not fit a compute unit (%zu B LDS)",
                         p->layer_lds);
-        p->layer_grid = std::min(layer_tasks(p->la), per_cu * cus);
+        p->layer_grid = std::min(layer_tasks(A.la), per_cu * cus);
     }
     p->ready = true;
     return MOE_OK;
 }
 
-void* gateup_args(moe_decode_plan_s* p) { return p->select_in_gateup ? (void*)&p->sga : (void*)&p->ga; }
+void* gateup_args(moe_decode_plan_s* p, Launches& A) { return p->select_in_gateup ? (void*)&A.sga : (void*)&A.ga; }
 
 moe_status launch(const KernelPick& k, void* args, hipStream_t s) {
     void* a[] = {args};
@@ -510,11 +531,11 @@ moe_status launch(const KernelPick& k, void* args, hipStream_t s) {
 
 // Eager launch on the caller's stream (and, in shared_stream mode, the plan's
 // second stream).  ev: per-slot start/end events for timing, or null.
-moe_status enqueue_eager(moe_decode_plan_s* p, hipStream_t stream, hipEvent_t* ev) {
+moe_status enqueue_eager(moe_decode_plan_s* p, Launches& A, hipStream_t stream, hipEvent_t* ev) {
     moe_status st;
     if (p->fused) {
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_LAYER], stream));
-        if ((st = launch(p->kl, &p->la, stream))) return st;
+        if ((st = launch(A.kl, &A.la, stream))) return st;
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_LAYER + 1], stream));
         return MOE_OK;
     }
@@ -523,28 +544,28 @@ moe_status enqueue_eager(moe_decode_plan_s* p, hipStream_t stream, hipEvent_t* e
         HIP_TRY(hipEventRecord(p->ev_fork, stream));
         HIP_TRY(hipStreamWaitEvent(p->s2, p->ev_fork, 0));
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_SHARED], p->s2));
-        if ((st = launch(p->ks, &p->gs, p->s2))) return st;
+        if ((st = launch(A.ks, &A.fa.s, p->s2))) return st;
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_SHARED + 1], p->s2));
         HIP_TRY(hipEventRecord(p->ev_join, p->s2));
     }
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT], stream));
-    if ((st = launch(p->kf, &p->fa, stream))) return st;
+    if ((st = launch(A.kf, &A.fa, stream))) return st;
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT + 1], stream));
     if (topk_own_launch(p)) {
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_TOPK], stream));
-        if ((st = launch(p->kt, &p->ta, stream))) return st;
+        if ((st = launch(A.kt, &A.ta, stream))) return st;
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_TOPK + 1], stream));
     }
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_GATEUP], stream));
-    if ((st = launch(p->kg, gateup_args(p), stream))) return st;
+    if ((st = launch(A.kg, gateup_args(p, A), stream))) return st;
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_GATEUP + 1], stream));
     if (side) HIP_TRY(hipStreamWaitEvent(stream, p->ev_join, 0));
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_DOWN], stream));
-    if ((st = launch(p->kd, p->expert_major ? (void*)&p->dx : (void*)&p->da, stream))) return st;
+    if ((st = launch(A.kd, p->expert_major ? (void*)&A.dx : (void*)&A.da, stream))) return st;
     if (ev) HIP_TRY(hipEventRecord(ev[2 * S_DOWN + 1], stream));
     if (p->expert_major) {
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_COMBINE], stream));
-        if ((st = launch(p->kc, &p->dx, stream))) return st;
+        if ((st = launch(A.kc, &A.dx, stream))) return st;
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_COMBINE + 1], stream));
     }
     return MOE_OK;
@@ -562,41 +583,42 @@ hipKernelNodeParams node_params(const KernelPick& k, void** args) {
 }
 
 moe_status build_graph(moe_decode_plan_s* p) {
+    Launches& A = p->m;
     HIP_TRY(hipGraphCreate(&p->graph, 0));
     if (p->fused) {
-        void* al[] = {&p->la};
-        hipKernelNodeParams np = node_params(p->kl, al);
+        void* al[] = {&A.la};
+        hipKernelNodeParams np = node_params(A.kl, al);
         HIP_TRY(hipGraphAddKernelNode(&p->n_layer, p->graph, nullptr, 0, &np));
         HIP_TRY(hipGraphInstantiate(&p->exec, p->graph, nullptr, nullptr, 0));
         return MOE_OK;
     }
-    void* af[] = {&p->fa};
-    void* ar[] = {&p->ta};
-    void* ag[] = {gateup_args(p)};
-    void* as[] = {&p->gs};
-    void* ad[] = {p->expert_major ? (void*)&p->dx : (void*)&p->da};
-    void* ac[] = {&p->dx};
-    hipKernelNodeParams np = node_params(p->kf, af);
+    void* af[] = {&A.fa};
+    void* ar[] = {&A.ta};
+    void* ag[] = {gateup_args(p, A)};
+    void* as[] = {&A.fa.s};
+    void* ad[] = {p->expert_major ? (void*)&A.dx : (void*)&A.da};
+    void* ac[] = {&A.dx};
+    hipKernelNodeParams np = node_params(A.kf, af);
     HIP_TRY(hipGraphAddKernelNode(&p->n_front, p->graph, nullptr, 0, &np));
     hipGraphNode_t route_done = p->n_front;
     if (topk_own_launch(p)) {
-        np = node_params(p->kt, ar);
+        np = node_params(A.kt, ar);
         HIP_TRY(hipGraphAddKernelNode(&p->n_topk, p->graph, &p->n_front, 1, &np));
         route_done = p->n_topk;
     }
-    np = node_params(p->kg, ag);
+    np = node_params(A.kg, ag);
     HIP_TRY(hipGraphAddKernelNode(&p->n_gateup, p->graph, &route_done, 1, &np));
     hipGraphNode_t deps[2] = {p->n_gateup, nullptr};
     int ndeps = 1;
     if (has_shared(p) && p->shared_stream) {
-        np = node_params(p->ks, as);
+        np = node_params(A.ks, as);
         HIP_TRY(hipGraphAddKernelNode(&p->n_shared, p->graph, nullptr, 0, &np));
         deps[ndeps++] = p->n_shared;
     }
-    np = node_params(p->kd, ad);
+    np = node_params(A.kd, ad);
     HIP_TRY(hipGraphAddKernelNode(&p->n_down, p->graph, deps, ndeps, &np));
     if (p->expert_major) {
-        np = node_params(p->kc, ac);
+        np = node_params(A.kc, ac);
         HIP_TRY(hipGraphAddKernelNode(&p->n_combine, p->graph, &p->n_down, 1, &np));
     }
     HIP_TRY(hipGraphInstantiate(&p->exec, p->graph, nullptr, nullptr, 0));
@@ -604,34 +626,35 @@ moe_status build_graph(moe_decode_plan_s* p) {
 }
 
 moe_status patch_graph(moe_decode_plan_s* p) {
+    Launches& A = p->m;
     if (p->fused) {
-        void* al[] = {&p->la};
-        hipKernelNodeParams np = node_params(p->kl, al);
+        void* al[] = {&A.la};
+        hipKernelNodeParams np = node_params(A.kl, al);
         HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_layer, &np));
         return MOE_OK;
     }
-    void* af[] = {&p->fa};
-    void* ar[] = {&p->ta};
-    void* ag[] = {gateup_args(p)};
-    void* as[] = {&p->gs};
-    void* ad[] = {p->expert_major ? (void*)&p->dx : (void*)&p->da};
-    void* ac[] = {&p->dx};
-    hipKernelNodeParams np = node_params(p->kf, af);
+    void* af[] = {&A.fa};
+    void* ar[] = {&A.ta};
+    void* ag[] = {gateup_args(p, A)};
+    void* as[] = {&A.fa.s};
+    void* ad[] = {p->expert_major ? (void*)&A.dx : (void*)&A.da};
+    void* ac[] = {&A.dx};
+    hipKernelNodeParams np = node_params(A.kf, af);
     HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_front, &np));
     if (topk_own_launch(p)) {
-        np = node_params(p->kt, ar);
+        np = node_params(A.kt, ar);
         HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_topk, &np));
     }
-    np = node_params(p->kg, ag);
+    np = node_params(A.kg, ag);
     HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_gateup, &np));
     if (has_shared(p) && p->shared_stream) {
-        np = node_params(p->ks, as);
+        np = node_params(A.ks, as);
         HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_shared, &np));
     }
-    np = node_params(p->kd, ad);
+    np = node_params(A.kd, ad);
     HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_down, &np));
     if (p->expert_major) {
-        np = node_params(p->kc, ac);
+        np = node_params(A.kc, ac);
         HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_combine, &np));
     }
     return MOE_OK;
@@ -644,6 +667,20 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 bool misaligned(const void* p) { return reinterpret_cast<uintptr_t>(p) & 15; }
+
+moe_status check_forward_args(const moe_decode_plan_s* p, const void* x, const void* router_w,
+                              const void* expert_w, const void* shared_w, const void* out) {
+    if (!p) return fail(MOE_ERR_INVALID, "plan is NULL");
+    const moe_decode_config& c = p->cfg;
+    if (!x || !router_w || !expert_w || !out || (c.shared_inter > 0 && !shared_w))
+        return fail(MOE_ERR_INVALID, "NULL tensor pointer");
+    if (misaligned(x) || misaligned(router_w) || misaligned(expert_w) || misaligned(out) ||
+        (c.shared_inter > 0 && misaligned(shared_w)))
+        return fail(MOE_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+    const size_t act_bytes = (size_t)c.batch * c.hidden * 2;
+    if (overlaps(x, act_bytes, out, act_bytes)) return fail(MOE_ERR_INVALID, "out overlaps x");
+    return MOE_OK;
+}
 
 }  // namespace
 
@@ -778,33 +815,28 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
 moe_status moe_decode_forward(moe_decode_plan_t p, const void* x, const void* router_w,
                               const void* expert_w, const void* shared_w, void* out, void* stream_) {
     g_err.clear();
-    if (!p) return fail(MOE_ERR_INVALID, "plan is NULL");
-    const moe_decode_config& c = p->cfg;
-    if (!x || !router_w || !expert_w || !out || (c.shared_inter > 0 && !shared_w))
-        return fail(MOE_ERR_INVALID, "NULL tensor pointer");
-    if (misaligned(x) || misaligned(router_w) || misaligned(expert_w) || misaligned(out) ||
-        (c.shared_inter > 0 && misaligned(shared_w)))
-        return fail(MOE_ERR_INVALID, "tensor pointers must be 16-byte aligned");
-    const size_t act_bytes = (size_t)c.batch * c.hidden * 2;
-    if (overlaps(x, act_bytes, out, act_bytes)) return fail(MOE_ERR_INVALID, "out overlaps x");
+    moe_status st = check_forward_args(p, x, router_w, expert_w, shared_w, out);
+    if (st) return st;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     HIP_TRY(hipStreamIsCapturing(stream, &cap));
     if (cap == hipStreamCaptureStatusActive && !p->ready)
         return fail(MOE_ERR_STATE, "the first forward of a plan allocates and zeroes its workspace; "
                     "run it outside stream capture");
-    moe_status st = device_init(p, stream);
+    st = device_init(p, stream);
     if (st) return st;
     if (!has_shared(p)) shared_w = nullptr;
     const void* tuple[5] = {x, router_w, expert_w, shared_w, out};
-    if (!p->have_forward || std::memcmp(tuple, p->args_for, sizeof tuple) != 0) {
-        set_pointers(p, x, router_w, expert_w, shared_w, out);
+    if (!p->m_valid || std::memcmp(tuple, p->args_for, sizeof tuple) != 0) {
+        set_pointers(p, p->m, x, router_w, expert_w, shared_w, out);
         std::memcpy(p->args_for, tuple, sizeof tuple);
+        p->m_valid = true;
     }
     p->have_forward = true;
     p->last_stream = stream;
+    p->last_ws = p->ws;
 
-    if (cap == hipStreamCaptureStatusActive) return enqueue_eager(p, stream, nullptr);  // into the caller's graph
+    if (cap == hipStreamCaptureStatusActive) return enqueue_eager(p, p->m, stream, nullptr);  // into the caller's graph
     if (p->profiling) {
         if (p->prof_count >= kMaxProfiledForwards)
             return fail(MOE_ERR_STATE, "profiling records at most %d forwards", kMaxProfiledForwards);
@@ -814,7 +846,7 @@ moe_status moe_decode_forward(moe_decode_plan_t p, const void* x, const void* ro
             HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableSystemFence));
             p->prof_events.push_back(ev);
         }
-        st = enqueue_eager(p, stream, &p->prof_events[base]);
+        st = enqueue_eager(p, p->m, stream, &p->prof_events[base]);
         if (st) return st;
         ++p->prof_count;
         return MOE_OK;
@@ -832,6 +864,46 @@ moe_status moe_decode_forward(moe_decode_plan_t p, const void* x, const void* ro
     return MOE_OK;
 }
 
+moe_status moe_decode_forward_noalloc(moe_decode_plan_t p, const void* x, const void* router_w,
+                                      const void* expert_w, const void* shared_w, void* out, void* stream_) {
+    g_err.clear();
+    moe_status st = check_forward_args(p, x, router_w, expert_w, shared_w, out);
+    if (st) return st;
+    if (p->fused)
+        return fail(MOE_ERR_UNSUPPORTED, "the allocation-free forward runs the staged launches; this plan "
+                    "asks for the single launch (single_launch = 2)");
+    if (has_shared(p) && p->shared_stream)
+        return fail(MOE_ERR_UNSUPPORTED, "the allocation-free forward runs on the caller's stream only; this "
+                    "plan puts the shared expert on a second stream (shared_stream = 1)");
+    void* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    HIP_TRY(scratch_for_current_device(&scratch, &scratch_bytes));
+    if (p->L.total > scratch_bytes)
+        return fail(MOE_ERR_UNSUPPORTED, "the plan needs %zu bytes of scratch; the allocation-free forward "
+                    "has %zu", p->L.total, scratch_bytes);
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (!has_shared(p)) shared_w = nullptr;
+    const void* tuple[5] = {x, router_w, expert_w, shared_w, out};
+    char* ws = static_cast<char*>(scratch);
+    if (p->na_ws != ws) {
+        fill_static_args(p, ws, p->na, true);
+        p->na_ws = ws;
+        set_pointers(p, p->na, x, router_w, expert_w, shared_w, out);
+        std::memcpy(p->na_for, tuple, sizeof tuple);
+    } else if (std::memcmp(tuple, p->na_for, sizeof tuple) != 0) {
+        set_pointers(p, p->na, x, router_w, expert_w, shared_w, out);
+        std::memcpy(p->na_for, tuple, sizeof tuple);
+    }
+    // the scratch holds whatever the device's last call left: clear the
+    // counters and split-K partials and write the shared expert's work list
+    if ((st = launch(p->na.ki, &p->na.ia, stream))) return st;
+    if ((st = enqueue_eager(p, p->na, stream, nullptr))) return st;
+    p->have_forward = true;
+    p->last_stream = stream;
+    p->last_ws = ws;
+    return MOE_OK;
+}
+
 moe_status moe_decode_routing(moe_decode_plan_t p, int32_t* topk_idx, float* topk_w, int32_t* n_unique,
                               float* logits, void* stream_) {
     g_err.clear();
@@ -839,12 +911,13 @@ moe_status moe_decode_routing(moe_decode_plan_t p, int32_t* topk_idx, float* top
     if (!p->have_forward) return fail(MOE_ERR_STATE, "no forward has run on this plan");
     hipStream_t s = static_cast<hipStream_t>(stream_);
     const size_t n = (size_t)p->cfg.batch * p->cfg.top_k;
-    if (topk_idx) HIP_TRY(hipMemcpyAsync(topk_idx, p->ws + p->L.topk_idx, n * 4, hipMemcpyDeviceToDevice, s));
-    if (topk_w) HIP_TRY(hipMemcpyAsync(topk_w, p->ws + p->L.topk_w, n * 4, hipMemcpyDeviceToDevice, s));
+    const char* ws = p->last_ws;
+    if (topk_idx) HIP_TRY(hipMemcpyAsync(topk_idx, ws + p->L.topk_idx, n * 4, hipMemcpyDeviceToDevice, s));
+    if (topk_w) HIP_TRY(hipMemcpyAsync(topk_w, ws + p->L.topk_w, n * 4, hipMemcpyDeviceToDevice, s));
     if (n_unique)
-        HIP_TRY(hipMemcpyAsync(n_unique, p->ws + p->L.meta + 4 * M_NACT, 4, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync(n_unique, ws + p->L.meta + 4 * M_NACT, 4, hipMemcpyDeviceToDevice, s));
     if (logits)
-        HIP_TRY(hipMemcpyAsync(logits, p->ws + p->L.z, (size_t)p->cfg.batch * p->cfg.n_experts * 4,
+        HIP_TRY(hipMemcpyAsync(logits, ws + p->L.z, (size_t)p->cfg.batch * p->cfg.n_experts * 4,
                                hipMemcpyDeviceToDevice, s));
     return MOE_OK;
 }
@@ -860,7 +933,7 @@ moe_status moe_decode_read_stats(moe_decode_plan_t p, moe_decode_stats* stats) {
     HIP_TRY(hipStreamSynchronize(p->last_stream));
     if (p->s2) HIP_TRY(hipStreamSynchronize(p->s2));
     int32_t meta[M_COUNT];
-    HIP_TRY(hipMemcpy(meta, p->ws + p->L.meta, sizeof meta, hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(meta, p->last_ws + p->L.meta, sizeof meta, hipMemcpyDeviceToHost));
     stats->n_unique = meta[M_NACT];
     stats->gemv_tiles = meta[M_GEMV_TILES];
     stats->mfma_tiles = meta[M_MFMA_TILES];

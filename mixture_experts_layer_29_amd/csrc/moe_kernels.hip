@@ -37,6 +37,8 @@
 // hand-off data is only read after the counter was seen, and only static
 // weights are loaded before that (article Part 2 section 3 reports a compiler
 // hoisting activation loads above a wait as a real bug).
+#include <algorithm>
+
 #include "moe_device.h"
 
 namespace moe {
@@ -862,15 +864,19 @@ __global__ __launch_bounds__(128) void combine_kernel(DownXArgs a) {
     *reinterpret_cast<uint2*>(a.out + (size_t)t * H + r) = uint2{o0, o1};
 }
 
-__global__ void init_lists_kernel(InitArgs a) {
+__global__ __launch_bounds__(256) void init_lists_kernel(InitArgs a) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     if (t < a.B) a.sh_perm[t] = t;
+    if (t < M_COUNT && a.zero_meta) a.meta[t] = t == M_SHARED_NACT ? 1 : 0;
     if (t == 0) {
-        a.meta[M_SHARED_NACT] = 1;
+        if (!a.zero_meta) a.meta[M_SHARED_NACT] = 1;
         a.sh_act_e[0] = 0;
         a.sh_act_off[0] = 0;
         a.sh_act_off[1] = a.B;
     }
+    const long long n4 = a.zero_words / 4;
+    for (long long i = t; i < n4; i += (long long)gridDim.x * blockDim.x)
+        reinterpret_cast<u32x4*>(a.zero)[i] = u32x4{0, 0, 0, 0};
 }
 
 // ---------------------------------------------------------------------------
@@ -886,7 +892,9 @@ static int tb_bucket(int b) {
 #define MOE_FN(f) reinterpret_cast<const void*>(&f)
 
 KernelPick pick_init(const InitArgs& a) {
-    return {MOE_FN(init_lists_kernel), dim3((a.B + 63) / 64), dim3(64), 0};
+    const long long need = std::max<long long>({(long long)a.B, (long long)M_COUNT, a.zero_words / 4});
+    const long long grid = std::min<long long>(1024, (need + 255) / 256);
+    return {MOE_FN(init_lists_kernel), dim3((unsigned)grid), dim3(256), 0};
 }
 
 int front_router_blocks(const RouterArgs& a) { return (a.E + 3) / 4; }
