@@ -108,10 +108,10 @@ def cpu_model() -> str:
 class Line:
     """One workload line: a plan, its layers and activation batches."""
 
-    def __init__(self, name, wl, batch, layers, xs, bias=None, flush=False, latency_only=False):
+    def __init__(self, name, wl, batch, layers, xs, bias=None, flush=False, latency_only=False, prefetch=False):
         self.name, self.wl, self.batch = name, wl, batch
         self.layers, self.xs, self.bias = layers, xs, bias
-        self.flush, self.latency_only = flush, latency_only
+        self.flush, self.latency_only, self.prefetch = flush, latency_only, prefetch
 
 
 def run_line(moe, torch, ln: Line, steps, warmup, replays, flush_buf=None) -> dict:
@@ -126,7 +126,12 @@ def run_line(moe, torch, ln: Line, steps, warmup, replays, flush_buf=None) -> di
 
     def step(i, record=None):
         ly = ln.layers[i % L]
-        plan.forward(ln.xs[i % X], ly["router_w"], ly["expert_w"], ly["shared_w"], outs[i % X])
+        if ln.prefetch:  # the next step's layer: its router and shared weights are prefetched
+            nx = ln.layers[(i + 1) % L]
+            plan.forward_prefetch(ln.xs[i % X], ly["router_w"], ly["expert_w"], ly["shared_w"], outs[i % X],
+                                  nx["router_w"], nx["shared_w"])
+        else:
+            plan.forward(ln.xs[i % X], ly["router_w"], ly["expert_w"], ly["shared_w"], outs[i % X])
         if record is not None:
             plan.routing(None, None, nu[record:record + 1], None)
 
@@ -207,6 +212,7 @@ def run_line(moe, torch, ln: Line, steps, warmup, replays, flush_buf=None) -> di
     kernel_us = {k: (v[0] * 1e3 / v[1]) for k, v in prof.items() if v[1]}
     res = {
         "workload": ln.name,
+        "prefetch_next_layer": ln.prefetch,
         "shape": {"hidden": wl.hidden, "n_experts": wl.n_experts, "top_k": wl.top_k, "inter": wl.inter,
                   "shared_inter": wl.shared_inter, "score": "softmax" if wl.score_fn == 0 else "sigmoid",
                   "router_std": wl.router_std, "zipf_s": wl.zipf_s if ln.bias is not None else None},
@@ -423,10 +429,13 @@ def main():
             {k: round(v, 2) for k, v in r["kernel_us"].items()}))
         return r
 
-    head = run(Line("tp8_b1", wl, 1, layers, xs_for(wl, 1)))
+    # headline: batch 1 with the next layer's router and shared weights
+    # prefetched during the selection; the same without prefetch beside it
+    head = run(Line("tp8_b1", wl, 1, layers, xs_for(wl, 1), prefetch=True))
+    run(Line("tp8_b1_noprefetch", wl, 1, layers, xs_for(wl, 1)))
     for name in want:
         kind, b = name.rsplit("_b", 1)
-        b = int(b)
+        b = int(b.split("_")[0])
         if kind == "tp8":
             run(Line(name, wl, b, layers, xs_for(wl, b)))
         elif kind == "spec":

@@ -102,8 +102,19 @@ typedef struct moe_decode_config {
                                 default mfma_min_tokens that is what it does; a
                                 mfma_min_tokens <= batch keeps 0 at 1, and asking
                                 for 3 with it fails with MOE_ERR_UNSUPPORTED        */
-    int32_t single_launch;   /* 0 (default) or 1: the staged launches.  2: the whole
-                                layer as ONE persistent launch -- possible when
+    int32_t single_launch;   /* 0 (default): the library's choice.  At batch 1, where
+                                the shape has a batch-1 experts kernel (H <= 8192,
+                                k * I <= 2048, Is a multiple of 128 up to 512) and
+                                the device holds its grid (k * I / 4 workgroups,
+                                two per CU: 512 at the TP8 shard) resident at once,
+                                two launches: the router (+ the shared expert's
+                                gate/up), then the routed experts, shared down and
+                                combine in ONE launch whose workgroups hand h over
+                                through per-expert counters (the Kimi K3 decode
+                                article, Part 1 section 2: producer and consumer
+                                fused at small batch); otherwise the staged
+                                launches.  1: the staged launches always.  2: the
+                                whole layer as ONE persistent launch -- possible when
                                 batch <= 4, shared_stream = 0, topk_launch != 2 and
                                 the shape fits it (x and h staged in LDS), else
                                 MOE_ERR_UNSUPPORTED at plan time.  On MI355X it
@@ -128,8 +139,13 @@ typedef struct moe_decode_info {
     int32_t shared_mfma;      /* 1 if the shared expert runs on MFMA tiles              */
     int32_t shared_stream;    /* resolved shared_stream                                  */
     int32_t router_mfma;      /* 1: router is a split-K MFMA launch + a top-k launch     */
-    int32_t single_launch;    /* 1: the layer runs as one persistent launch             */
-    int32_t layer_grid;       /* its workgroup count (0 until the first forward)        */
+    int32_t single_launch;    /* 0: staged launches; 1: the layer runs as one persistent
+                                 launch (single_launch = 2 in the config); 2: batch 1
+                                 as router launch + one experts launch (before the
+                                 first forward this assumes the device holds its
+                                 grid; the first forward checks, else 0)           */
+    int32_t layer_grid;       /* the persistent grid's workgroup count (0 until the
+                                 first forward)                                         */
     int32_t topk_launch;      /* resolved top-k placement: 1, 2 or 3 (see the config),
                                  0 with the single launch                              */
     size_t workspace_bytes;   /* device workspace owned by the plan                     */
@@ -188,6 +204,22 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
 moe_status moe_decode_forward(moe_decode_plan_t plan, const void* x, const void* router_w,
                               const void* expert_w, const void* shared_w, void* out,
                               void* stream);
+
+/* moe_decode_forward, plus a cross-layer prefetch: while the layer selects its
+ * experts (a phase that leaves HBM mostly idle) it reads the NEXT layer's
+ * router weight (bf16 [E][H]) and shared expert weights (the shared_w layout)
+ * with ordinary cached loads and drops them, so the next layer's router and
+ * shared expert find them in the 256 MB Infinity Cache.  Source: the Kimi K3
+ * decode article, Part 1 section 4 (prefetching future weights into the cache
+ * from a phase that cannot use the memory bandwidth).  Either next pointer may
+ * be NULL (nothing of it is prefetched); they are only read.  Issued by the
+ * batch-1 experts launch (moe_decode_plan_info: single_launch = 2); the other
+ * launch forms ignore the next-layer pointers.  Errors as moe_decode_forward,
+ * plus MOE_ERR_INVALID for a misaligned next pointer. */
+moe_status moe_decode_forward_prefetch(moe_decode_plan_t plan, const void* x, const void* router_w,
+                                       const void* expert_w, const void* shared_w, void* out,
+                                       const void* next_router_w, const void* next_shared_w,
+                                       void* stream);
 
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe_decode.so")
 HEADER = os.path.join(_ROOT, "include", "moe_decode.h")
 _CSRC = os.path.join(_HERE, "csrc")
 SOURCES = [os.path.join(_CSRC, f) for f in ("moe_kernels.hip", "moe_layer_tb1.hip", "moe_layer_tb2.hip",
-                                             "moe_layer_tb4.hip", "moe_scratch.hip", "moe_decode.cpp")]
+                                             "moe_layer_tb4.hip", "moe_scratch.hip", "moe_fused.hip",
+                                             "moe_decode.cpp")]
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_NOMEM, MOE_ERR_STATE = range(6)
 STATUS_NAMES = ["MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP", "MOE_ERR_NOMEM",
@@ -28,7 +29,8 @@ VARIANT_AUTO, VARIANT_SMALL_M, VARIANT_SPLIT_K = 0, 1, 2
 VARIANT_NAMES = {0: "AUTO", 1: "SMALL_M", 2: "SPLIT_K"}
 SINGLE_AUTO, SINGLE_OFF, SINGLE_REQUIRED = 0, 1, 2
 
-EXPORTS = ["moe_decode_plan", "moe_decode_forward", "moe_decode_forward_noalloc", "moe_decode_routing",
+EXPORTS = ["moe_decode_plan", "moe_decode_forward", "moe_decode_forward_prefetch", "moe_decode_forward_noalloc",
+           "moe_decode_routing",
            "moe_decode_read_stats",
            "moe_decode_plan_info", "moe_decode_set_profiling", "moe_decode_profile_read",
            "moe_decode_destroy", "moe_decode_last_error"]
@@ -103,6 +105,7 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_plan.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(P)]
         L.moe_decode_forward.argtypes = [P, P, P, P, P, P, P]
         L.moe_decode_forward_noalloc.argtypes = [P, P, P, P, P, P, P]
+        L.moe_decode_forward_prefetch.argtypes = [P, P, P, P, P, P, P, P, P]
         L.moe_decode_routing.argtypes = [P, P, P, P, P, P]
         L.moe_decode_read_stats.argtypes = [P, ctypes.POINTER(Stats)]
         L.moe_decode_plan_info.argtypes = [P, ctypes.POINTER(Info)]
@@ -168,6 +171,12 @@ class Plan:
                                         _ptr(shared_w), _ptr(out), _stream(stream)))
         return out
 
+    def forward_prefetch(self, x, router_w, expert_w, shared_w, out, next_router_w, next_shared_w, stream=None):
+        _check(lib().moe_decode_forward_prefetch(self.handle, _ptr(x), _ptr(router_w), _ptr(expert_w),
+                                                 _ptr(shared_w), _ptr(out), _ptr(next_router_w),
+                                                 _ptr(next_shared_w), _stream(stream)))
+        return out
+
     def forward_noalloc(self, x, router_w, expert_w, shared_w, out, stream=None):
         _check(lib().moe_decode_forward_noalloc(self.handle, _ptr(x), _ptr(router_w), _ptr(expert_w),
                                                 _ptr(shared_w), _ptr(out), _stream(stream)))
@@ -191,7 +200,7 @@ class Plan:
         _check(lib().moe_decode_set_profiling(self.handle, 1 if enable else 0))
 
     def profile_read(self) -> dict:
-        cap = 8
+        cap = 16
         ms = (ctypes.c_double * cap)()
         cnt = (ctypes.c_int32 * cap)()
         names = (ctypes.c_char_p * cap)()

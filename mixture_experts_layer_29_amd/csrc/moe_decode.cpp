@@ -14,7 +14,7 @@
 // pointers change; a forward on a capturing stream launches the kernels
 // directly so they land in the caller's graph.  The eager path is also used
 // for per-kernel timing.
-#include "../../include/moe_decode.h"
+#include "moe_decode.h"
 
 #include <hip/hip_runtime.h>
 
@@ -68,9 +68,9 @@ constexpr size_t kDownHLds = 48 * 1024;   // output-stationary down: h fully sta
 constexpr int kDownOsMaxBatch = 4;        // output-stationary down up to this batch, expert-major above  // dynamic LDS of the single launch: x staging, then h rows
 
 enum Slot { S_FRONT = 0, S_TOPK = 1, S_GATEUP = 2, S_SHARED = 3, S_DOWN = 4, S_LAYER = 5, S_COMBINE = 6,
-            S_COUNT = 7 };
+            S_EXPERTS = 7, S_COUNT = 8 };
 const char* kSlotNames[S_COUNT] = {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine",
-                                   "layer", "combine"};
+                                   "layer", "combine", "experts_b1"};
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -85,13 +85,16 @@ struct Launches {
     DownXArgs dx{};       // expert-major down of the staged launches
     LayerArgs la{};
     InitArgs ia{};        // per-call set-up of the allocation-free forward
-    KernelPick kf{}, kt{}, kg{}, ks{}, kd{}, kl{}, kc{}, ki{};
+    FusedArgs fb{};       // batch 1: the routed experts, shared down and combine in one launch
+    FrontArgs fbf{};      // batch 1: its router launch (router rows, shared gate/up pairs, sync re-arm)
+    KernelPick kf{}, kt{}, kg{}, ks{}, kd{}, kl{}, kc{}, ki{}, kb{}, kbf{};
 };
 
 struct Layout {
     size_t meta, z, zacc, topk_idx, topk_w, act_e, act_off, perm, sh_act_e, sh_act_off, sh_perm;
     size_t h, hs, g_acc, g_acc_s, tile_cnt, tile_cnt_s, s_out, part, part_s, spart, total;
-    size_t zero_end;  // [g_acc, zero_end): split-K partials and tile counters, zero between uses
+    size_t sync;      // counters and flags of the batch-1 experts launch
+    size_t zero_end;  // [sync, zero_end): counters, flags, split-K partials and tile counters, zero between uses
 };
 
 }  // namespace
@@ -111,7 +114,9 @@ struct moe_decode_plan_s {
     bool select_in_router;// batch <= 4: top-k + bucketing in the router's last workgroup
     bool select_in_gateup;// batch <= 4: every routed gate/up workgroup selects and buckets
     bool shared_in_gateup;// that form also runs the shared gate/up row pairs (one per workgroup)
-    bool fused;           // the whole layer as one persistent launch
+    bool fused;           // the whole layer as one persistent launch (batch <= 4, on request)
+    bool fused_b1;        // batch 1: the whole layer as one launch (fused_b1_kernel)
+    int fb_grid = 0;      // its workgroups on this device (0 until resolved)
     bool expert_major;    // staged down: expert-major tiles + combine launch (else output-stationary)
     size_t layer_lds;     // its dynamic LDS bytes
     int layer_grid = 0;   // its workgroups (set on the first forward)
@@ -128,7 +133,7 @@ struct moe_decode_plan_s {
     // static scratch array (na, the allocation-free forward)
     Launches m{}, na{};
     char* na_ws = nullptr;      // the scratch the na blocks point into
-    const void* na_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    const void* na_for[7] = {};
     const char* last_ws = nullptr;  // workspace of the last forward (routing / stats read it)
 
     // graph
@@ -136,8 +141,9 @@ struct moe_decode_plan_s {
     hipGraphExec_t exec = nullptr;
     hipGraphNode_t n_front = nullptr, n_topk = nullptr, n_gateup = nullptr, n_shared = nullptr,
                    n_down = nullptr, n_layer = nullptr, n_combine = nullptr;
-    const void* args_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // in the arg blocks
-    const void* graph_for[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};  // in the graph exec
+    // x, router_w, expert_w, shared_w, out, next router_w, next shared_w
+    const void* args_for[7] = {};   // in the arg blocks
+    const void* graph_for[7] = {};  // in the graph exec
     bool have_forward = false;
     bool m_valid = false;  // the m blocks hold the pointers in args_for
     hipStream_t last_stream = nullptr;  // the stream of the last forward
@@ -155,6 +161,36 @@ bool has_shared(const moe_decode_plan_s* p) { return p->cfg.shared_inter > 0; }
 bool topk_own_launch(const moe_decode_plan_s* p) { return !p->select_in_router && !p->select_in_gateup; }
 // the shared expert's gate/up in trailing workgroups of the front launch
 bool shared_in_front(const moe_decode_plan_s* p) { return has_shared(p) && !p->shared_stream; }
+
+
+// The batch-1 single launch needs all of its workgroups resident at once: its
+// grid against what the occupancy allows on the current device.  Falls back
+// to the staged launches (fused_b1 = false) where they do not fit.
+moe_status resolve_fused_b1(moe_decode_plan_s* p) {
+    if (!p->fused_b1 || p->fb_grid) return MOE_OK;
+    const moe_decode_config& c = p->cfg;
+    FusedArgs f{};
+    f.H = c.hidden;
+    f.E = c.n_experts;
+    f.k = c.top_k;
+    f.I = c.inter;
+    f.Is = c.shared_inter;
+    const KernelPick k = pick_fused_b1(f, 1 << 30);
+    if (!k.func) {
+        p->fused_b1 = false;
+        return MOE_OK;
+    }
+    int dev = 0, per_cu = 0, cus = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.func, 256, 0));
+    HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    if ((long long)per_cu * cus < (long long)k.grid.x) {
+        p->fused_b1 = false;
+        return MOE_OK;
+    }
+    p->fb_grid = (int)k.grid.x;
+    return MOE_OK;
+}
 
 moe_status validate(const moe_decode_config* c) {
     if (!c) return fail(MOE_ERR_INVALID, "config is NULL");
@@ -222,15 +258,14 @@ Layout make_layout(const moe_decode_config& c, int max_act, bool split, bool fus
     L.sh_perm = take(B * 4);
     L.h = take(B * k * I * 4);
     L.hs = take(B * (Is ? Is : 1) * 4);
+    L.sync = take((size_t)kSyncWords * 4);
     if (split) {
         L.g_acc = take(B * k * 2 * I * 4);
         L.g_acc_s = take(B * 2 * (Is ? Is : 1) * 4);
         L.tile_cnt = take((size_t)max_act * (I / kPairsPerMfmaTile) * 4);
         L.tile_cnt_s = take((Is / kPairsPerMfmaTile + 1) * 4);
-        L.zero_end = o;
-    } else {
-        L.g_acc = L.zero_end = o;
     }
+    L.zero_end = o;
     if (fused && Is) L.s_out = take(B * c.hidden * 4);
     if (expert_major) {  // per-pair / per-shared-block partials of the expert-major down
         L.part = take(B * k * c.hidden * 4);
@@ -254,8 +289,8 @@ void fill_static_args(moe_decode_plan_s* p, char* ws, Launches& A, bool clear) {
     const bool split = p->variant == MOE_VARIANT_SPLIT_K;
     A.ia = InitArgs{at<int32_t>(ws, p->L.meta), at<int32_t>(ws, p->L.sh_act_e), at<int32_t>(ws, p->L.sh_act_off),
                     at<int32_t>(ws, p->L.sh_perm), c.batch, clear ? 1 : 0,
-                    clear ? at<uint32_t>(ws, p->L.g_acc) : nullptr,
-                    clear ? (long long)((p->L.zero_end - p->L.g_acc) / 4) : 0};
+                    clear ? at<uint32_t>(ws, p->L.sync) : nullptr,
+                    clear ? (long long)((p->L.zero_end - p->L.sync) / 4) : 0};
     A.ki = pick_init(A.ia);
     RouterArgs& r = A.fa.r;
     r.bias = c.router_bias;
@@ -345,6 +380,30 @@ void fill_static_args(moe_decode_plan_s* p, char* ws, Launches& A, bool clear) {
     A.ta.nspart = p->L.spart ? p->dks : 0;
     A.ta.sel_blocks = (c.batch + 3) / 4;
 
+    {
+        FusedArgs& f = A.fb;
+        f.z = at<float>(ws, p->L.z);
+        f.h = at<float>(ws, p->L.h);
+        f.hs = at<float>(ws, p->L.hs);
+        f.sync = at<int32_t>(ws, p->L.sync);
+        f.topk_idx = r.topk_idx;
+        f.topk_w = r.topk_w;
+        f.meta = r.meta;
+        f.act_e = r.act_e;
+        f.act_off = r.act_off;
+        f.perm = r.perm;
+        f.H = c.hidden;
+        f.E = c.n_experts;
+        f.k = c.top_k;
+        f.I = c.inter;
+        f.Is = c.shared_inter;
+        f.score_fn = c.score_fn;
+        f.renormalize = c.renormalize;
+        f.routed_scale = c.routed_scale;
+        f.add_residual = c.add_residual;
+        f.rows = p->fb_grid ? (c.hidden + p->fb_grid - 1) / p->fb_grid : 0;
+    }
+
     DownArgs& d = A.da;
     d.n_act = g.n_act;
     d.act_e = r.act_e;
@@ -403,7 +462,8 @@ void fill_static_args(moe_decode_plan_s* p, char* ws, Launches& A, bool clear) {
 int layer_tasks(const LayerArgs& l) { return l.n_router + l.n_sgu + l.n_sdown + l.n_gu + l.n_down; }
 
 void set_pointers(moe_decode_plan_s* p, Launches& A, const void* x, const void* router_w, const void* expert_w,
-                  const void* shared_w, void* out) {
+                  const void* shared_w, void* out, const void* next_router_w = nullptr,
+                  const void* next_shared_w = nullptr) {
     const moe_decode_config& c = p->cfg;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const uint16_t* ew = static_cast<const uint16_t*>(expert_w);
@@ -422,6 +482,27 @@ void set_pointers(moe_decode_plan_s* p, Launches& A, const void* x, const void* 
     A.dx.w2 = A.da.w2;
     A.dx.s2 = A.da.s2;
     A.dx.out = A.da.out;
+    if (p->fused_b1) {
+        FusedArgs& f = A.fb;
+        f.x = xb;
+        f.w13 = ew;
+        f.w2 = A.da.w2;
+        f.s2 = A.da.s2;
+        f.out = A.da.out;
+        f.pf_a = static_cast<const uint16_t*>(next_router_w);
+        f.pf_a_units = next_router_w ? (long long)c.n_experts * c.hidden / 8 : 0;
+        f.pf_b = has_shared(p) ? static_cast<const uint16_t*>(next_shared_w) : nullptr;
+        f.pf_b_units = f.pf_b ? 3LL * c.shared_inter * c.hidden / 8 : 0;
+        A.kb = pick_fused_b1(f, p->fb_grid);
+        // its router launch: one router row per workgroup, then one shared
+        // gate/up row pair per workgroup; workgroup 0 re-arms the sync block
+        A.fbf = A.fa;
+        A.fbf.router_blocks = c.n_experts;
+        A.fbf.shared_blocks = has_shared(p) ? c.shared_inter : 0;
+        A.fbf.sync_clear = f.sync;
+        A.fbf.sync_words = kSyncWords;
+        A.kbf = pick_front_split(A.fbf);
+    }
     if (p->select_in_gateup) {
         A.sga.r = A.fa.r;
         A.sga.g = A.ga;
@@ -497,6 +578,8 @@ moe_status device_init_once(moe_decode_plan_s* p, hipStream_t stream, int dev) {
     // zero once: counters re-arm themselves and split-K partials are cleared after use
     HIP_TRY(hipMemsetAsync(p->ws, 0, p->L.total, stream));
     Launches& A = p->m;
+    moe_status st = resolve_fused_b1(p);
+    if (st) return st;
     fill_static_args(p, p->ws, A, false);
     {
         void* args[] = {&A.ia};
@@ -533,6 +616,15 @@ moe_status launch(const KernelPick& k, void* args, hipStream_t s) {
 // second stream).  ev: per-slot start/end events for timing, or null.
 moe_status enqueue_eager(moe_decode_plan_s* p, Launches& A, hipStream_t stream, hipEvent_t* ev) {
     moe_status st;
+    if (p->fused_b1) {
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT], stream));
+        if ((st = launch(A.kbf, &A.fbf, stream))) return st;
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT + 1], stream));
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_EXPERTS], stream));
+        if ((st = launch(A.kb, &A.fb, stream))) return st;
+        if (ev) HIP_TRY(hipEventRecord(ev[2 * S_EXPERTS + 1], stream));
+        return MOE_OK;
+    }
     if (p->fused) {
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_LAYER], stream));
         if ((st = launch(A.kl, &A.la, stream))) return st;
@@ -585,6 +677,16 @@ hipKernelNodeParams node_params(const KernelPick& k, void** args) {
 moe_status build_graph(moe_decode_plan_s* p) {
     Launches& A = p->m;
     HIP_TRY(hipGraphCreate(&p->graph, 0));
+    if (p->fused_b1) {
+        void* af[] = {&A.fbf};
+        void* ae[] = {&A.fb};
+        hipKernelNodeParams np = node_params(A.kbf, af);
+        HIP_TRY(hipGraphAddKernelNode(&p->n_front, p->graph, nullptr, 0, &np));
+        np = node_params(A.kb, ae);
+        HIP_TRY(hipGraphAddKernelNode(&p->n_layer, p->graph, &p->n_front, 1, &np));
+        HIP_TRY(hipGraphInstantiate(&p->exec, p->graph, nullptr, nullptr, 0));
+        return MOE_OK;
+    }
     if (p->fused) {
         void* al[] = {&A.la};
         hipKernelNodeParams np = node_params(A.kl, al);
@@ -627,6 +729,15 @@ moe_status build_graph(moe_decode_plan_s* p) {
 
 moe_status patch_graph(moe_decode_plan_s* p) {
     Launches& A = p->m;
+    if (p->fused_b1) {
+        void* af[] = {&A.fbf};
+        void* ae[] = {&A.fb};
+        hipKernelNodeParams np = node_params(A.kbf, af);
+        HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_front, &np));
+        np = node_params(A.kb, ae);
+        HIP_TRY(hipGraphExecKernelNodeSetParams(p->exec, p->n_layer, &np));
+        return MOE_OK;
+    }
     if (p->fused) {
         void* al[] = {&A.la};
         hipKernelNodeParams np = node_params(A.kl, al);
@@ -804,6 +915,21 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
     }
     p->shared_in_gateup = p->select_in_gateup && shared_in_front(p) &&
                           c.shared_inter <= p->max_act * (c.inter / kPairsPerGemvTile);
+    // Batch 1: the whole layer as one launch where the shape has a batch-1
+    // kernel (GEMV tiles only: no MFMA threshold the batch reaches), unless
+    // the caller asks for another form.  Whether its grid fits the device is
+    // checked at the first forward (else the staged launches run).
+    {
+        FusedArgs f{};
+        f.H = c.hidden;
+        f.E = c.n_experts;
+        f.k = c.top_k;
+        f.I = c.inter;
+        f.Is = c.shared_inter;
+        p->fused_b1 = c.batch == 1 && !p->fused && c.single_launch == 0 && !p->shared_stream &&
+                      c.topk_launch == 0 && !p->shared_mfma && (p->mfma_min == 0 || p->mfma_min > 1) &&
+                      pick_fused_b1(f, 1 << 30).func != nullptr;
+    }
     p->expert_major = c.batch > kDownOsMaxBatch;
     p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K, p->fused, p->expert_major,
                        p->small_router ? 1 : p->dks_r,
@@ -812,11 +938,14 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
     return MOE_OK;
 }
 
-moe_status moe_decode_forward(moe_decode_plan_t p, const void* x, const void* router_w,
-                              const void* expert_w, const void* shared_w, void* out, void* stream_) {
+moe_status moe_decode_forward_prefetch(moe_decode_plan_t p, const void* x, const void* router_w,
+                                       const void* expert_w, const void* shared_w, void* out,
+                                       const void* next_router_w, const void* next_shared_w, void* stream_) {
     g_err.clear();
     moe_status st = check_forward_args(p, x, router_w, expert_w, shared_w, out);
     if (st) return st;
+    if (misaligned(next_router_w) || misaligned(next_shared_w))
+        return fail(MOE_ERR_INVALID, "next-layer pointers must be 16-byte aligned");
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     HIP_TRY(hipStreamIsCapturing(stream, &cap));
@@ -826,9 +955,10 @@ moe_status moe_decode_forward(moe_decode_plan_t p, const void* x, const void* ro
     st = device_init(p, stream);
     if (st) return st;
     if (!has_shared(p)) shared_w = nullptr;
-    const void* tuple[5] = {x, router_w, expert_w, shared_w, out};
+    if (!has_shared(p)) next_shared_w = nullptr;
+    const void* tuple[7] = {x, router_w, expert_w, shared_w, out, next_router_w, next_shared_w};
     if (!p->m_valid || std::memcmp(tuple, p->args_for, sizeof tuple) != 0) {
-        set_pointers(p, p->m, x, router_w, expert_w, shared_w, out);
+        set_pointers(p, p->m, x, router_w, expert_w, shared_w, out, next_router_w, next_shared_w);
         std::memcpy(p->args_for, tuple, sizeof tuple);
         p->m_valid = true;
     }
@@ -864,6 +994,11 @@ moe_status moe_decode_forward(moe_decode_plan_t p, const void* x, const void* ro
     return MOE_OK;
 }
 
+moe_status moe_decode_forward(moe_decode_plan_t p, const void* x, const void* router_w,
+                              const void* expert_w, const void* shared_w, void* out, void* stream) {
+    return moe_decode_forward_prefetch(p, x, router_w, expert_w, shared_w, out, nullptr, nullptr, stream);
+}
+
 moe_status moe_decode_forward_noalloc(moe_decode_plan_t p, const void* x, const void* router_w,
                                       const void* expert_w, const void* shared_w, void* out, void* stream_) {
     g_err.clear();
@@ -875,6 +1010,7 @@ moe_status moe_decode_forward_noalloc(moe_decode_plan_t p, const void* x, const 
     if (has_shared(p) && p->shared_stream)
         return fail(MOE_ERR_UNSUPPORTED, "the allocation-free forward runs on the caller's stream only; this "
                     "plan puts the shared expert on a second stream (shared_stream = 1)");
+    if ((st = resolve_fused_b1(p))) return st;
     void* scratch = nullptr;
     size_t scratch_bytes = 0;
     HIP_TRY(scratch_for_current_device(&scratch, &scratch_bytes));
@@ -883,7 +1019,7 @@ moe_status moe_decode_forward_noalloc(moe_decode_plan_t p, const void* x, const 
                     "has %zu", p->L.total, scratch_bytes);
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (!has_shared(p)) shared_w = nullptr;
-    const void* tuple[5] = {x, router_w, expert_w, shared_w, out};
+    const void* tuple[7] = {x, router_w, expert_w, shared_w, out, nullptr, nullptr};
     char* ws = static_cast<char*>(scratch);
     if (p->na_ws != ws) {
         fill_static_args(p, ws, p->na, true);
@@ -945,18 +1081,18 @@ moe_status moe_decode_plan_info(moe_decode_plan_t p, moe_decode_info* info) {
     g_err.clear();
     if (!p || !info) return fail(MOE_ERR_INVALID, "NULL argument");
     info->variant = p->variant;
-    info->n_kernels = p->fused ? 1
+    info->n_kernels = p->fused ? 1 : p->fused_b1 ? 2
                       : 3 + (topk_own_launch(p) ? 1 : 0) + (has_shared(p) && p->shared_stream ? 1 : 0) +
                             (p->expert_major ? 1 : 0);
-    info->topk_launch = p->fused ? 0 : p->select_in_gateup ? 3 : p->select_in_router ? 1 : 2;
+    info->topk_launch = p->fused || p->fused_b1 ? 0 : p->select_in_gateup ? 3 : p->select_in_router ? 1 : 2;
     info->mfma_min_tokens = p->mfma_min;
     info->shared_mfma = p->shared_mfma ? 1 : 0;
     info->shared_stream = p->shared_stream ? 1 : 0;
     info->router_mfma = p->small_router ? 0 : 1;
-    info->single_launch = p->fused ? 1 : 0;
-    info->layer_grid = p->layer_grid;
+    info->single_launch = p->fused ? 1 : p->fused_b1 ? 2 : 0;
+    info->layer_grid = p->fused_b1 ? p->fb_grid : p->layer_grid;
     info->workspace_bytes = p->L.total;
-    info->shared_gateup_in = !has_shared(p) ? 0 : p->fused ? 4 : p->shared_stream ? 3
+    info->shared_gateup_in = !has_shared(p) ? 0 : p->fused ? 4 : p->fused_b1 ? 1 : p->shared_stream ? 3
                              : p->shared_in_gateup ? 2 : 1;
     return MOE_OK;
 }
@@ -988,9 +1124,10 @@ moe_status moe_decode_profile_read(moe_decode_plan_t p, int32_t cap, double* tot
     if (p->prof_count == 0) return MOE_OK;
     for (int f = 0; f < p->prof_count; ++f) {
         for (int s = 0; s < S_COUNT && s < cap; ++s) {
-            const bool used = p->fused ? s == S_LAYER
+            const bool used = p->fused_b1 ? (s == S_FRONT || s == S_EXPERTS)
+                              : p->fused ? s == S_LAYER
                               : !((s == S_SHARED && !(has_shared(p) && p->shared_stream)) ||
-                                  (s == S_TOPK && !topk_own_launch(p)) || s == S_LAYER ||
+                                  (s == S_TOPK && !topk_own_launch(p)) || s == S_LAYER || s == S_EXPERTS ||
                                   (s == S_COMBINE && !p->expert_major));
             if (!used) continue;
             hipEvent_t a = p->prof_events[((size_t)f * S_COUNT + s) * 2];

@@ -244,6 +244,8 @@ template <int TB>
 __global__ __launch_bounds__(256) void front_split_kernel(FrontArgs f) {
     const RouterArgs& a = f.r;
     const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && f.sync_clear)  // re-arms the next launch's counters and flags
+        for (int i = tid; i < f.sync_words; i += 256) f.sync_clear[i] = 0;
     if ((int)blockIdx.x < f.router_blocks) {
         __shared__ float s_part[4][1][TB];
         const int e = blockIdx.x;

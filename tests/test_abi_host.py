@@ -134,17 +134,16 @@ def test_auto_variant(batch, variant):
     # (+ shared gate/up), top-k launch, routed gate/up, expert-major down,
     # combine
     big = 1 if batch > 4 else 0
-    sel_gu = batch == 1
+    one = batch == 1  # batch 1: the whole layer as one launch (grid checked at the first forward)
     assert info.router_mfma == big
-    assert info.single_launch == 0
-    assert info.n_kernels == 3 + 2 * big
-    assert info.topk_launch == (2 if big else 3 if sel_gu else 1)
+    assert info.single_launch == (2 if one else 0)
+    assert info.n_kernels == (2 if one else 3 + 2 * big)
+    assert info.topk_launch == (0 if one else 2 if big else 1)
     assert info.layer_grid == 0
     assert info.shared_stream == 0
-    # batch 1: the shared gate/up row pairs ride in the routed gate/up launch
-    assert info.shared_gateup_in == (2 if sel_gu else 1)
+    assert info.shared_gateup_in == 1
     assert info.workspace_bytes > 0
-    if sel_gu:  # every gate/up tile is a GEMV tile in that form
+    if one:  # every gate/up tile is a GEMV tile in that form
         assert info.mfma_min_tokens == 0 and info.shared_mfma == 0
     elif variant == moe.VARIANT_SPLIT_K:
         assert info.mfma_min_tokens == 5
@@ -159,6 +158,8 @@ def test_auto_variant(batch, variant):
     p.destroy()
     p = moe.Plan(cfg(batch=batch, single_launch=moe.SINGLE_OFF))
     assert p.info().n_kernels == 3 + 2 * big and p.info().single_launch == 0
+    if one:  # the staged form at batch 1: every gate/up workgroup selects for itself
+        assert p.info().topk_launch == 3 and p.info().shared_gateup_in == 2
     p.destroy()
     if batch <= 4:
         p = moe.Plan(cfg(batch=batch, single_launch=moe.SINGLE_REQUIRED))
@@ -178,7 +179,7 @@ def test_auto_variant(batch, variant):
 ])
 def test_single_launch_policy(kw, fused):
     p = moe.Plan(cfg(**kw))
-    assert p.info().single_launch == 0  # never the default
+    assert p.info().single_launch != 1  # the general persistent launch is never the default
     p.destroy()
     st = plan_status(cfg(single_launch=moe.SINGLE_REQUIRED, **kw))
     assert st == (moe.MOE_OK if fused else moe.MOE_ERR_UNSUPPORTED)
@@ -196,13 +197,16 @@ def test_topk_launch_policy(batch):
         i = p.info()
         p.destroy()
         return i
-    # by default every gate/up workgroup selects for itself only while the
-    # gate/up grid is one generation (batch 1 at this shape)
+    # by default batch 1 runs as one launch; with the staged launches every
+    # gate/up workgroup selects for itself only while the gate/up grid is one
+    # generation (batch 1 at this shape)
     default_tl = 3 if batch == 1 else 1
-    i = info()
+    i = info(single_launch=moe.SINGLE_OFF)
     assert i.topk_launch == default_tl and i.n_kernels == 3 and i.shared_mfma == 0
     if batch == 1:
         assert i.mfma_min_tokens == 0
+        i = info()
+        assert i.topk_launch == 0 and i.n_kernels == 2 and i.single_launch == 2
     i = info(topk_launch=3, shared_stream=1)
     assert i.topk_launch == 3 and i.n_kernels == 4
     i = info(topk_launch=1)
@@ -213,7 +217,7 @@ def test_topk_launch_policy(batch):
     i = info(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=1)
     assert i.topk_launch == 1 and i.mfma_min_tokens == 1 and i.shared_mfma == 1
     # one it cannot reach does not
-    i = info(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=batch + 1)
+    i = info(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=batch + 1, single_launch=moe.SINGLE_OFF)
     assert i.topk_launch == default_tl and i.shared_mfma == 0
     i = info(single_launch=moe.SINGLE_REQUIRED)
     assert i.topk_launch == 0 and i.n_kernels == 1
@@ -225,6 +229,25 @@ def test_auto_variant_falls_back_where_gemv_staging_does_not_fit(batch, variant)
     takes split-K tiles from batch 2 instead of refusing the shape."""
     p = moe.Plan(cfg(hidden=16384, batch=batch))
     assert p.info().variant == variant
+    p.destroy()
+
+
+@pytest.mark.parametrize("kw,one", [
+    (dict(), True),                                                      # TP8 shard
+    (dict(hidden=256, n_experts=8, top_k=2, inter=128, shared_inter=128), True),   # tiny
+    (dict(hidden=256, n_experts=8, top_k=8, inter=128, shared_inter=128), True),   # k = E
+    (dict(shared_inter=0), True),
+    (dict(inter=2048, shared_inter=2048), False),                        # unsharded: W2 rows do not fit
+    (dict(hidden=16384), False),                                         # more than 16 units per lane
+    (dict(shared_inter=64, inter=64), False),                            # Is not a multiple of 128
+    (dict(shared_stream=1), False), (dict(topk_launch=1), False),
+    (dict(single_launch=moe.SINGLE_OFF), False),
+    (dict(force_variant=moe.VARIANT_SPLIT_K, mfma_min_tokens=1), False),  # asks for MFMA tiles
+])
+def test_batch1_single_launch_policy(kw, one):
+    p = moe.Plan(cfg(batch=1, **kw))
+    i = p.info()
+    assert (i.single_launch == 2) == one and (i.n_kernels == 2) == one
     p.destroy()
 
 
@@ -250,7 +273,7 @@ def test_profiling_toggle_without_device():
     p.set_profiling(True)
     prof = p.profile_read()
     assert set(prof) == {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine", "layer",
-                         "combine"}
+                         "combine", "experts_b1"}
     assert all(v == (0.0, 0) for v in prof.values())
     p.set_profiling(False)
     p.destroy()

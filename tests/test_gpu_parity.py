@@ -83,7 +83,19 @@ def test_tp8_uniform(tp8, batch):
     shape = shape_of(synthetic.TP8)
     m, st, info = check(tp8, shape, batch, "tp8 B=%d" % batch)
     assert info.variant == (moe.VARIANT_SMALL_M if batch <= 2 else moe.VARIANT_SPLIT_K)
-    assert info.single_launch == 0
+    # batch 1: the router launch, then the routed experts, shared down and
+    # combine in one launch over a grid of 512 resident workgroups
+    assert info.single_launch == (2 if batch == 1 else 0)
+    if batch == 1:
+        assert info.n_kernels == 2 and info.layer_grid == 512
+
+
+def test_tp8_batch1_staged(tp8):
+    """Batch 1 with the staged launches (router, gate/up selecting for
+    itself, down), the form the single launch replaces."""
+    shape = shape_of(synthetic.TP8)
+    m, st, info = check(tp8, shape, 1, "tp8 B=1 staged", single_launch=moe.SINGLE_OFF)
+    assert info.single_launch == 0 and info.n_kernels == 3
 
 
 @pytest.mark.parametrize("topk_launch", [1, 2, 3])
@@ -127,6 +139,61 @@ def test_tp8_single_launch_variants(tp8, batch, kw):
     assert info.single_launch == 1
     if kw.get("mfma_min_tokens") == 1:
         assert st.mfma_tiles > 0 and st.gemv_tiles == 0
+
+
+@pytest.mark.parametrize("wl_name", ["tp8", "tiny"])
+def test_batch1_single_launch_agrees_with_staged_many_forwards(tp8, tiny, wl_name):
+    """Batch 1: the one-launch form against the staged launches over many
+    forwards with fresh inputs on one plan each.  Both are deterministic (GEMV
+    tiles, fixed summation orders), so each must repeat itself bit for bit,
+    and they differ only by fp32 summation order.  A counter that did not
+    re-arm, or a hand-off that read a previous forward's logits or h, breaks
+    one of the checks."""
+    layer = tp8 if wl_name == "tp8" else tiny
+    shape = shape_of(layer.wl)
+    one = make_plan(layer, shape, 1)
+    staged = make_plan(layer, shape, 1, single_launch=moe.SINGLE_OFF)
+    g = torch.Generator().manual_seed(4321)
+    for it in range(40):
+        x = (torch.randn(1, shape.hidden, generator=g) * (1 + it % 3)).to(torch.bfloat16).cuda()
+        o1, o2, o3 = (torch.empty_like(x) for _ in range(3))
+        one.forward(x, layer.router_w, layer.expert_w, layer.shared_w, o1)
+        one.forward(x, layer.router_w, layer.expert_w, layer.shared_w, o3)
+        staged.forward(x, layer.router_w, layer.expert_w, layer.shared_w, o2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)), "single launch %d not repeatable" % it
+        a, b = o1.float(), o2.float()
+        tol = torch.maximum(a.abs(), b.abs()) * 2.0 ** -7 + 2.0 ** -12 * float(b.square().mean().sqrt())
+        d = (a - b).abs()
+        assert bool((d <= tol).all()), "forward %d: forms differ: max %g" % (it, float(d.max()))
+    assert one.info().single_launch == 2 and one.info().n_kernels == 2
+    assert one.stats().error_flags == 0 and staged.stats().error_flags == 0
+    one.destroy()
+    staged.destroy()
+
+
+@pytest.mark.parametrize("batch", [1, 4, 16])
+def test_forward_with_next_layer_prefetch(tp8, tp8_unit, batch):
+    """The next layer's router and shared weights prefetched during the
+    selection (here another layer's, tp8_unit) change nothing in the result:
+    bit for bit the plain forward at batch <= 4 (deterministic paths), and the
+    oracle at the parity bar."""
+    shape = shape_of(synthetic.TP8)
+    x_bits, _ = gap_x(tp8, shape, batch, offset=1500)
+    x = synthetic.bits_to_torch_bf16(x_bits, "cuda")
+    plan = make_plan(tp8, shape, batch)
+    plain = torch.empty_like(x)
+    plan.forward(x, tp8.router_w, tp8.expert_w, tp8.shared_w, plain)
+    for rep in range(3):
+        out = torch.full_like(x, float("nan"))
+        plan.forward_prefetch(x, tp8.router_w, tp8.expert_w, tp8.shared_w, out, tp8_unit.router_w,
+                              tp8_unit.shared_w)
+        torch.cuda.synchronize()
+        if batch <= 4:
+            assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), "rep %d" % rep
+        compare_out(out, run_oracle(tp8, shape, x_bits)[0], "prefetch B=%d rep %d" % (batch, rep))
+    assert plan.stats().error_flags == 0
+    plan.destroy()
 
 
 @pytest.mark.parametrize("B", [1, 2, 3])
@@ -303,14 +370,15 @@ def test_forwards_captured_into_a_caller_graph(tp8, batch, shared_stream):
     plan.destroy()
 
 
-@pytest.mark.parametrize("B,slots", [
-    (16, {"front", "topk_bucket", "gateup_routed", "down_combine", "combine"}),
-    (1, {"front", "gateup_routed", "down_combine"}),
+@pytest.mark.parametrize("B,kw,slots", [
+    (16, {}, {"front", "topk_bucket", "gateup_routed", "down_combine", "combine"}),
+    (1, dict(single_launch=moe.SINGLE_OFF), {"front", "gateup_routed", "down_combine"}),
+    (1, {}, {"front", "experts_b1"}),
 ])
-def test_profiling_path_matches(tp8, B, slots):
+def test_profiling_path_matches(tp8, B, kw, slots):
     shape = shape_of(synthetic.TP8)
     x, _ = gap_x(tp8, shape, B, offset=300)
-    plan = make_plan(tp8, shape, B)
+    plan = make_plan(tp8, shape, B, **kw)
     plan.set_profiling(True)
     for _ in range(3):
         out, idx, w, nu = run_gpu(plan, tp8, x, shape)

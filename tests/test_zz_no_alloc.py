@@ -51,7 +51,8 @@ def tiny():
 
 
 def test_noalloc_matches_forward_on_consecutive_sizes(tp8, tiny):
-    cases = [(tp8, 16, 0), (tp8, 2, 40), (tiny, 8, 0), (tp8, 16, 80)]  # each smaller, then larger again
+    # sizes falling, then rising again; batch 1 runs as one launch
+    cases = [(tp8, 16, 0), (tp8, 2, 40), (tp8, 1, 60), (tiny, 8, 0), (tiny, 1, 20), (tp8, 16, 80), (tp8, 1, 90)]
     for layer, batch, offset in cases:
         shape = shape_of(layer.wl)
         label = "%s B=%d" % (layer.wl.name, batch)
