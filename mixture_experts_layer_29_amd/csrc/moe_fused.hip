@@ -67,13 +67,30 @@ __global__ __launch_bounds__(256, 2) void fused_b1_kernel(FusedArgs a) {
     const int b = blockIdx.x;
     const u32x4 zero = u32x4{0, 0, 0, 0};
 
-    // ------------------------------------------------ x, then the selection
+    // ------------------- x, the S2 rows and hs (static or from the router
+    // launch: they stream while the selection runs), then the selection
     u32x4 xr[UX];
 #pragma unroll
     for (int q = 0; q < UX; ++q) {
         const int u = tid + 256 * q;
         xr[q] = ld16(a.x + 8 * (u < units ? u : 0));
     }
+    // down rows: thread -> (row rr, lane-in-row l); its units are l + 16 q of
+    // the row's k * I / 8 routed units and of the row's Is / 8 shared units
+    const int rr = tid / kFusedRowThreads, l = tid % kFusedRowThreads;
+    const int row = b * a.rows + rr;
+    const bool row_ok = rr < a.rows && row < H;
+    const int rowc = row_ok ? row : 0;
+    const int nsu = Is >> 3;
+    u32x4 s2u[SP];
+#pragma unroll
+    for (int q = 0; q < SP; ++q) {
+        const int c = l + kFusedRowThreads * q;
+        const bool ok = row_ok && c < nsu;
+        s2u[q] = (Is > 0) ? ld16_stream(a.s2 + (size_t)rowc * Is + 8 * (ok ? c : 0)) : zero;
+    }
+    const bool hs_mine = tid < Is / 4;
+    const float4 hsv = *reinterpret_cast<const float4*>(a.hs + 4 * (hs_mine ? tid : 0));
     if (wave == 0) {
         float v[NS];
 #pragma unroll
@@ -147,9 +164,10 @@ __global__ __launch_bounds__(256, 2) void fused_b1_kernel(FusedArgs a) {
         const int u = tid + 256 * q;
         if (u < units) st16(s_x + 8 * u, xr[q]);
     }
+    if (hs_mine) reinterpret_cast<float4*>(s_hs)[tid] = hsv;
     __syncthreads();
 
-    // ------------------------ routed gate/up rows, then W2, S2 rows and hs
+    // --------- routed gate/up rows; h published; then the W2 rows requested
     // I is a power of two from 128 (the host checks): expert / unit indices
     // below are shifts, not divisions
     const int tiles_per = I / kPairsPerGemvTile, tsh = __builtin_ctz(tiles_per);
@@ -166,32 +184,8 @@ __global__ __launch_bounds__(256, 2) void fused_b1_kernel(FusedArgs a) {
         wg[q] = ld16_stream(grow + 8 * uc);
         wu[q] = ld16_stream(urow + 8 * uc);
     }
-    // down rows: thread -> (row rr, lane-in-row l); its units are l + 16 q of
-    // the row's k * I / 8 routed units and of the row's Is / 8 shared units.
-    // I / 8 is a multiple of 16, so unit q of every thread belongs to expert
-    // q >> qsh and column unit c = 16 (q & (qpe - 1)) + l
-    const int rr = tid / kFusedRowThreads, l = tid % kFusedRowThreads;
-    const int row = b * a.rows + rr;
-    const bool row_ok = rr < a.rows && row < H;
-    const int rowc = row_ok ? row : 0;
-    const int upr = I >> 3, qpe = upr / kFusedRowThreads, qsh = __builtin_ctz(qpe), nsu = Is >> 3;
-    const int nq = k * qpe;  // this thread's routed units
-    u32x4 w2u[UP], s2u[SP];
-#pragma unroll
-    for (int q = 0; q < UP; ++q) {
-        const bool ok = row_ok && q < nq;
-        const int j = ok ? q >> qsh : 0, c = ok ? kFusedRowThreads * (q & (qpe - 1)) + l : 0;
-        w2u[q] = ld16_stream(a.w2 + ((size_t)s_sel_e[j] * H + rowc) * I + 8 * c);
-    }
-#pragma unroll
-    for (int q = 0; q < SP; ++q) {
-        const int c = l + kFusedRowThreads * q;
-        const bool ok = row_ok && c < nsu;
-        s2u[q] = (Is > 0) ? ld16_stream(a.s2 + (size_t)rowc * Is + 8 * (ok ? c : 0)) : zero;
-    }
-    const bool hs_mine = tid < Is / 4;
-    const float4 hsv = *reinterpret_cast<const float4*>(a.hs + 4 * (hs_mine ? tid : 0));
     int32_t* cnt_j = a.sync + kSyncLineWords * j_t;
+    int arrived = 0;
     if (has_tile) {
         float ag = 0.0f, au = 0.0f;
 #pragma unroll
@@ -206,18 +200,29 @@ __global__ __launch_bounds__(256, 2) void fused_b1_kernel(FusedArgs a) {
         const float gs = wave_sum(ag), us = wave_sum(au);
         if (lane == 0) st_dev(a.h + (size_t)j_t * I + i_t, silu_f(gs) * us);
         stores_done_barrier();
-        if (tid == 0) {
-            const int t = __hip_atomic_fetch_add(cnt_j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (t == tiles_per - 1) {  // expert j complete: raise its flag in every replica
+        // counted now; its value is looked at once the W2 rows are requested
+        if (tid == 0) arrived = __hip_atomic_fetch_add(cnt_j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // W2 rows of the k selected experts (static weights): requested after the
+    // gate/up rows are consumed and h is counted, so the hand-off below runs
+    // while they stream.  I / 8 is a multiple of 16, so unit q of every thread
+    // belongs to expert q >> qsh and column unit c = 16 (q & (qpe - 1)) + l.
+    const int upr = I >> 3, qpe = upr / kFusedRowThreads, qsh = __builtin_ctz(qpe);
+    const int nq = k * qpe;  // this thread's routed units
+    u32x4 w2u[UP];
+#pragma unroll
+    for (int q = 0; q < UP; ++q) {
+        const bool ok = row_ok && q < nq;
+        const int j = ok ? q >> qsh : 0, c = ok ? kFusedRowThreads * (q & (qpe - 1)) + l : 0;
+        w2u[q] = ld16_stream(a.w2 + ((size_t)s_sel_e[j] * H + rowc) * I + 8 * c);
+    }
+    if (has_tile && tid == 0 && arrived == tiles_per - 1) {
+        // expert j complete: raise its flag in every replica
 #pragma unroll 1
-                for (int r = 0; r < kFlagReplicas; ++r) st_dev(a.sync + kSyncLineWords * (kMaxTopK + r) + j_t, 1);
-            }
-        }
+        for (int r = 0; r < kFlagReplicas; ++r) st_dev(a.sync + kSyncLineWords * (kMaxTopK + r) + j_t, 1);
     }
 
     // ----------------------------------------------------------------- down
-    if (hs_mine) reinterpret_cast<float4*>(s_hs)[tid] = hsv;
-    __syncthreads();
     float acc = 0.0f;
 #pragma unroll
     for (int q = 0; q < SP; ++q) {
