@@ -117,6 +117,7 @@ struct moe_decode_plan_s {
     bool fused;           // the whole layer as one persistent launch (batch <= 4, on request)
     bool fused_b1;        // batch 1: the whole layer as one launch (fused_b1_kernel)
     int fb_grid = 0;      // its workgroups on this device (0 until resolved)
+    int sel_grid = 0;     // select-in-gate/up form: workgroups the device holds at once (0 until known)
     bool expert_major;    // staged down: expert-major tiles + combine launch (else output-stationary)
     size_t layer_lds;     // its dynamic LDS bytes
     int layer_grid = 0;   // its workgroups (set on the first forward)
@@ -509,6 +510,16 @@ void set_pointers(moe_decode_plan_s* p, Launches& A, const void* x, const void* 
         A.sga.s = A.fa.s;
         A.kf = pick_front_split(A.fa);
         A.kg = pick_gateup_select(A.sga, p->max_act);
+        // a grid no larger than what the device holds at once: every workgroup
+        // selects once, then loops over its tiles
+        if (!p->sel_grid) {
+            int dev = 0, per_cu = 0, cus = 0;
+            if (hipGetDevice(&dev) == hipSuccess &&
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, A.kg.func, 256, A.kg.lds) == hipSuccess &&
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+                p->sel_grid = std::max(1, per_cu * cus);
+        }
+        if (p->sel_grid && (int)A.kg.grid.x > p->sel_grid) A.kg.grid.x = p->sel_grid;
     } else {
         A.kf = pick_front(A.fa, p->small_router, p->select_in_router, p->shared_mfma ? 0 : c.batch);
         if (topk_own_launch(p)) {
@@ -883,20 +894,17 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
             return fail(MOE_ERR_UNSUPPORTED, "single_launch = 2: %s", why);
         }
     }
-    // Batch <= 4: the selection can run in every routed gate/up workgroup
-    // (topk_launch 3).  That form runs every tile as a GEMV tile, so
-    // with the library's MFMA threshold it turns MFMA tiles off; a threshold
-    // the caller set that could reach MFMA tiles keeps the selection in the
-    // router's last workgroup (topk_launch 1) unless 3 is asked for.
-    // By default that form is taken only while the gate/up grid is one
-    // generation of workgroups (two per CU): every workgroup pays the
-    // selection before its weights, so a second generation pays it again.
-    // Measured on MI355X (TP8 shard): batch 1 (512 workgroups) 35.6 us in that
-    // form vs 39.0 us selecting in the router; batch 2 61.0 vs 58.8 us; batch 4
-    // 105.8 vs 93.2 us.
-    const bool one_generation = (size_t)p->max_act * (c.inter / kPairsPerGemvTile) <= kSelectGateupMaxTiles;
+    // Batch <= 4: the selection runs in every routed gate/up workgroup
+    // (topk_launch 3) by default.  That form runs every tile as a GEMV tile,
+    // so with the library's MFMA threshold it turns MFMA tiles off; a
+    // threshold the caller set that could reach MFMA tiles keeps the selection
+    // in the router's last workgroup (topk_launch 1) unless 3 is asked for.
+    // Its grid is capped at what the device holds at once and each workgroup
+    // loops over its tiles, so the selection is paid once per workgroup, not
+    // once per tile (a grid of one tile per workgroup, two generations at
+    // batch 2, measured 61.0 us against 58.8 us selecting in the router).
     p->select_in_gateup = false;
-    if (!p->fused && p->small_router && (c.topk_launch == 3 || (c.topk_launch == 0 && one_generation))) {
+    if (!p->fused && p->small_router && (c.topk_launch == 3 || c.topk_launch == 0)) {
         const bool gemv_only = !p->shared_mfma && (p->mfma_min == 0 || p->mfma_min > c.batch);
         if (gemv_only || c.mfma_min_tokens == 0) {
             p->select_in_gateup = true;
@@ -913,8 +921,12 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
         delete p;
         return fail(MOE_ERR_UNSUPPORTED, "topk_launch = 3 needs batch <= 4 with x in the LDS budget");
     }
+    // the shared expert's row pairs ride in the first gate/up workgroups (one
+    // pair each, streaming during their selection) where there are enough of
+    // them: the grid is the routed tiles, capped at one generation
     p->shared_in_gateup = p->select_in_gateup && shared_in_front(p) &&
-                          c.shared_inter <= p->max_act * (c.inter / kPairsPerGemvTile);
+                          (size_t)c.shared_inter <= std::min((size_t)p->max_act * (c.inter / kPairsPerGemvTile),
+                                                             kSelectGateupMaxTiles);
     // Batch 1: the whole layer as one launch where the shape has a batch-1
     // kernel (GEMV tiles only: no MFMA threshold the batch reaches), unless
     // the caller asks for another form.  Whether its grid fits the device is

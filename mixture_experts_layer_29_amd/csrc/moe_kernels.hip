@@ -272,8 +272,10 @@ __global__ __launch_bounds__(256) void front_split_kernel(FrontArgs f) {
 // Wave t < B selects token t's experts from z (the routing rows are written
 // by workgroup 0 only), wave 0 buckets the B*k pairs into LDS lists (and, in
 // workgroup 0, into the global lists the down launch reads), then the
-// workgroup runs tile `local` of entry `entry` with the entry's token ids from
-// LDS.  Every workgroup derives the same lists from the same logits.  At
+// workgroup runs routed tiles b, b + G, ... with each entry's token ids from
+// LDS.  Every workgroup derives the same lists from the same logits; the host
+// keeps the grid within what the device holds at once, so each workgroup pays
+// the selection once.  At
 // B = 1 the k experts are distinct, so pair j is entry j in slot j.
 // Workgroups b < shared_pairs also compute the shared expert's gate/up row
 // pair b: its loads go out right behind the logit loads, so they stream while
@@ -386,15 +388,20 @@ __global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
             sg.h[(size_t)tid * sg.n + b] = silu_f(gu[0]) * gu[1];
         }
     }
-    const int entry = b / g.tiles_per_expert, local = b % g.tiles_per_expert;
-    if (entry >= uni(s_nact)) return;
-    const int e = uni(s_act_e[entry]), off = uni(s_act_off[entry]);
-    const int T = uni(s_act_off[entry + 1]) - off;
-    if (T > TB) {  // an expert holds at most one pair per token, so T <= B <= TB
-        if (tid == 0 && local == 0) atomicOr(&g.meta[M_ERR], ERR_TILE);
-        return;
+    // the routed tiles, grid-strided: the grid is at most what the device
+    // holds at once, so each workgroup selects once for all its tiles
+    const int ntiles = uni(s_nact) * g.tiles_per_expert;
+    for (int tile = b; tile < ntiles; tile += gridDim.x) {
+        const int entry = tile / g.tiles_per_expert, local = tile % g.tiles_per_expert;
+        const int e = uni(s_act_e[entry]), off = uni(s_act_off[entry]);
+        const int T = uni(s_act_off[entry + 1]) - off;
+        if (T > TB) {  // an expert holds at most one pair per token, so T <= B <= TB
+            if (tid == 0 && local == 0) atomicOr(&g.meta[M_ERR], ERR_TILE);
+            continue;
+        }
+        gemv_gateup_tile<TB>(g, g.w + (size_t)e * (size_t)g.expert_stride, off, T, local, s_x, s_tok + off);
+        __syncthreads();  // the next tile restages s_x
     }
-    gemv_gateup_tile<TB>(g, g.w + (size_t)e * (size_t)g.expert_stride, off, T, local, s_x, s_tok + off);
 }
 
 // ---------------------------------------------------------------------------

@@ -138,12 +138,15 @@ def test_auto_variant(batch, variant):
     assert info.router_mfma == big
     assert info.single_launch == (2 if one else 0)
     assert info.n_kernels == (2 if one else 3 + 2 * big)
-    assert info.topk_launch == (0 if one else 2 if big else 1)
+    # batch 2-4: every gate/up workgroup selects for itself (a grid of at most
+    # one generation, looping over the tiles), the shared expert's row pairs
+    # in the first gate/up workgroups; above: a top-k launch
+    assert info.topk_launch == (0 if one else 2 if big else 3)
     assert info.layer_grid == 0
     assert info.shared_stream == 0
-    assert info.shared_gateup_in == 1
+    assert info.shared_gateup_in == (1 if one or big else 2)
     assert info.workspace_bytes > 0
-    if one:  # every gate/up tile is a GEMV tile in that form
+    if not big:  # batch <= 4: every gate/up tile is a GEMV tile in these forms
         assert info.mfma_min_tokens == 0 and info.shared_mfma == 0
     elif variant == moe.VARIANT_SPLIT_K:
         assert info.mfma_min_tokens == 5
@@ -200,7 +203,7 @@ def test_topk_launch_policy(batch):
     # by default batch 1 runs as one launch; with the staged launches every
     # gate/up workgroup selects for itself only while the gate/up grid is one
     # generation (batch 1 at this shape)
-    default_tl = 3 if batch == 1 else 1
+    default_tl = 3
     i = info(single_launch=moe.SINGLE_OFF)
     assert i.topk_launch == default_tl and i.n_kernels == 3 and i.shared_mfma == 0
     if batch == 1:
