@@ -56,11 +56,12 @@ METRIC = "MoE decode layer µs & tokens/s at batch 1/16/64; achieved HBM GB/s vs
 # HBM traffic of the batch-1 launches (rocprofv3 FETCH_SIZE x 2.0 and
 # WRITE_SIZE x 1.0 KiB per dispatch, the scales a 2 GiB device copy gives
 # those counters), taken on the kernel sources with these SHA-1s and reported
-# only while the sources are unchanged.  Filled in from
-# profiles/layer_tp8shard_b1_hbm_traffic.md.
-B1_TRAFFIC = None
+# only while the sources are unchanged (profiles/layer_tp8shard_b1_hbm_traffic.md).
+B1_TRAFFIC = {"kernels": {"front": (6360.7, 28.0), "experts_b1": (45036.7, 112.2)},
+              "fetch_scale": 2.0, "write_scale": 1.0,
+              "sources": {'moe_fused.hip': '3cb4841998349b1a913f896a54b38572c9df49bd', 'moe_kernels.hip': 'b4ab2d098ae53118dc94e4dda2726bea0164235b', 'moe_device.h': 'a68d097bde31ec7214ddf8816a5abe073a9e7b21', 'moe_args.h': '91e31570da8b9bd650ae48c274f51ffded8e0cb9'}}
 
-DEFAULT_LINES = ("tp8_b2,tp8_b4,tp8_b8,tp8_b16,tp8_b64,unit_b8,unit_b16,zipf_b64,spec_b8,spec_b64,"
+DEFAULT_LINES = ("tp8_b1_prefetch,tp8_b2,tp8_b4,tp8_b8,tp8_b16,tp8_b64,unit_b8,unit_b16,zipf_b64,spec_b8,spec_b64,"
                  "tiny_b1,full_b1,full_b16,full_b32,full_b64")
 
 
@@ -429,15 +430,16 @@ def main():
             {k: round(v, 2) for k, v in r["kernel_us"].items()}))
         return r
 
-    # headline: batch 1 with the next layer's router and shared weights
-    # prefetched during the selection; the same without prefetch beside it
-    head = run(Line("tp8_b1", wl, 1, layers, xs_for(wl, 1), prefetch=True))
-    run(Line("tp8_b1_noprefetch", wl, 1, layers, xs_for(wl, 1)))
+    # headline: batch 1 (plain forward)
+    head = run(Line("tp8_b1", wl, 1, layers, xs_for(wl, 1)))
     for name in want:
         kind, b = name.rsplit("_b", 1)
-        b = int(b.split("_")[0])
+        b, _, variant = b.partition("_")
+        b = int(b)
         if kind == "tp8":
-            run(Line(name, wl, b, layers, xs_for(wl, b)))
+            # the *_prefetch line also prefetches the next step's router and
+            # shared weights (moe_decode_forward_prefetch)
+            run(Line(name, wl, b, layers, xs_for(wl, b), prefetch=variant == "prefetch"))
         elif kind == "spec":
             run(Line(name, wl, b, layers, xs_for(wl, b, spec=True)))
         elif kind == "zipf":
@@ -501,6 +503,10 @@ def main():
         "gateup_routed": float(sum(2 * 2 * wl.hidden * wl.inter * int(u) for u in nu1)) / len(nu1)
         + (sh_gu if head["_shared_gateup_in"] == 2 else 0),
         "down_combine": float(sum(2 * wl.hidden * wl.inter * int(u) for u in nu1)) / len(nu1)
+        + 2 * wl.hidden * wl.shared_inter,
+        # batch 1, one launch after the router launch: routed gate/up and down
+        # rows and the shared expert's down rows
+        "experts_b1": float(sum(2 * 3 * wl.hidden * wl.inter * int(u) for u in nu1)) / len(nu1)
         + 2 * wl.hidden * wl.shared_inter,
         "layer": head["weight_bytes_mean"],
     }.get(dom)
