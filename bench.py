@@ -532,6 +532,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "replays": args.replays,
+        "timed_steps_total": head["timed_steps"],
         "ms_per_step": head["layer_us"] / 1e3,
         "ms_per_step_p10": head["layer_us_p10"] / 1e3,
         "ms_per_step_p90": head["layer_us_p90"] / 1e3,
