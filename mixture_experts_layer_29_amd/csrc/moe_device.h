@@ -378,39 +378,62 @@ __device__ __forceinline__ void bucket_meta(const RouterArgs& a, int nact, int n
 // number of pairs with a smaller (expert, pair) key, so slots are ordered by
 // expert then token.  The first pair of each expert leads; entries (active
 // experts) are numbered in expert order (apos) and an entry's slots start at
-// its lead's slot.  cnt: the expert's pair count.
+// its lead's slot; cnt (set for leads) is the expert's pair count.
+//
+// Runs in one wave with 128 ints of LDS (s_ps) of its own: every lane writes
+// its unique key (expert * 64 + lane) to LDS and counts the smaller keys from
+// broadcast reads of all of them (a rank, so the keys' sorted positions), then
+// scatters its key to its sorted position; neighbours in sorted order give the
+// leads, a ballot of the leads gives apos and cnt.  LDS accesses of one wave
+// complete in issue order, so the compiler-only fences are all the ordering
+// this needs.  (A loop of per-lane readlanes instead cost ~5 us for 64 pairs.)
 struct PairSlot {
     int pos, apos, cnt;
     bool lead;
 };
-__device__ __forceinline__ PairSlot pair_slot(int e, int np, int lane) {
-    PairSlot r{0, 0, 0, false};
-    bool first = true;
-    for (int q = 0; q < np; ++q) {
-        const int eq = __builtin_amdgcn_readlane(e, q);
-        r.pos += (eq < e || (eq == e && q < lane)) ? 1 : 0;
-        r.cnt += eq == e ? 1 : 0;
-        if (eq == e && q < lane) first = false;
+__device__ __forceinline__ PairSlot pair_slot(int e, int np, int lane, int32_t* s_ps) {
+    constexpr int kPad = 1 << 20;  // above every expert id (E <= 1024)
+    const bool act = lane < np;
+    const int key = (act ? e : kPad) * 64 + lane;
+    s_ps[lane] = key;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    int pos = 0;
+    const int4* k4 = reinterpret_cast<const int4*>(s_ps);
+    const int nq = (np + 15) >> 4;
+    for (int q = 0; q < nq; ++q) {
+        int4 v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = k4[4 * q + c];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            pos += (v[c].x < key ? 1 : 0) + (v[c].y < key ? 1 : 0) + (v[c].z < key ? 1 : 0) + (v[c].w < key ? 1 : 0);
     }
-    r.lead = lane < np && first;
-    const unsigned long long fm = __ballot(r.lead);
-    for (int q = 0; q < np; ++q) {
-        const int eq = __builtin_amdgcn_readlane(e, q);
-        r.apos += (((fm >> q) & 1ull) && eq < e) ? 1 : 0;
+    if (act) s_ps[64 + pos] = key;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int cur = act ? s_ps[64 + lane] >> 6 : -1;
+    const int prev = (act && lane > 0) ? s_ps[63 + lane] >> 6 : -1;
+    const unsigned long long lm = __ballot(act && cur != prev);  // leads, by sorted position
+    PairSlot r{0, 0, 0, false};
+    if (act) {
+        r.pos = pos;
+        r.lead = (lm >> pos) & 1ull;
+        r.apos = __popcll(lm & ((1ull << pos) - 1ull));
+        const unsigned long long above = pos < 63 ? (lm >> (pos + 1)) << (pos + 1) : 0ull;
+        r.cnt = (above ? __ffsll(above) - 1 : np) - pos;
     }
     return r;
 }
 
 // Bucketing by one wave for B*k <= 64 pairs (pair p in lane p) into the
 // global work lists (see pair_slot).  No barriers and no LDS atomics.
-__device__ __forceinline__ void bucket_wave(const RouterArgs& a, const int32_t* s_pair_e, int lane) {
+__device__ __forceinline__ void bucket_wave(const RouterArgs& a, const int32_t* s_pair_e, int lane, int32_t* s_ps) {
     const int np = a.B * a.k;
     const int e = lane < np ? s_pair_e[lane] : kNone;
     if (__ballot(lane < np && (e < 0 || e >= a.E))) {  // never hand an invalid id to the experts
         if (lane == 0) bucket_meta(a, 0, 0, np, -1);
         return;
     }
-    const PairSlot ps = pair_slot(e, np, lane);
+    const PairSlot ps = pair_slot(e, np, lane, s_ps);
     if (lane < np) st_dev(a.perm + ps.pos, lane);
     if (ps.lead) {
         st_dev(a.act_e + ps.apos, e);

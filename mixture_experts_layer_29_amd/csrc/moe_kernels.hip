@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void front_small_kernel(FrontArgs f) {
         return;
     }
     __shared__ int32_t s_pair_e[4 * kMaxTopK];
+    __shared__ __align__(16) int32_t s_ps[128];
     __shared__ int s_flag;
 
     router_rows<TB, SELECT>(a, blockIdx.x, s_x);
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void front_small_kernel(FrontArgs f) {
     if (!arrive_last(reinterpret_cast<unsigned*>(&a.meta[M_ROUTER_CNT]), f.router_blocks, &s_flag)) return;
 
     select_tokens<NS>(a, 0, a.z, nullptr, false, s_pair_e);
-    if ((threadIdx.x >> 6) == 0) bucket_wave(a, s_pair_e, threadIdx.x & 63);
+    if ((threadIdx.x >> 6) == 0) bucket_wave(a, s_pair_e, threadIdx.x & 63, s_ps);
 }
 
 // Dense split-K front (batch > 4): router tiles, then the shared expert's
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(256) void topk_bucket_kernel(TopkArgs ta) {
     __shared__ int32_t s_cnt[kMaxExperts];
     __shared__ int32_t s_tmp[8];
     __shared__ int32_t s_nmfma;
+    __shared__ __align__(16) int32_t s_ps[128];
     __shared__ int s_flag;
     const RouterArgs& a = ta.r;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -135,8 +137,8 @@ __global__ __launch_bounds__(256) void topk_bucket_kernel(TopkArgs ta) {
         for (int p = tid; p < np; p += 256) s_pair_e[p] = ld_dev(a.topk_idx + p);
         __syncthreads();
     }
-    if (np <= 64) {
-        if (wave == 0) bucket_wave(a, s_pair_e, lane);
+    if (np <= 32) {
+        if (wave == 0) bucket_wave(a, s_pair_e, lane, s_ps);
     } else {
         bucket_block(a, s_pair_e, s_rank, s_cnt, s_tmp, &s_nmfma);
     }
@@ -288,6 +290,7 @@ __global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
     __shared__ int32_t s_act_e[4 * kMaxTopK];
     __shared__ int32_t s_act_off[4 * kMaxTopK + 1];
     __shared__ int32_t s_nact;
+    __shared__ __align__(16) int32_t s_ps[128];
     __shared__ float s_part[4][2][TB];
     const RouterArgs& a = sa.r;
     const GateUpArgs& g = sa.g;
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
         if (__ballot(lane < np && (e < 0 || e >= a.E))) {  // never hand an invalid id to the experts
             if (out && lane == 0) bucket_meta(a, 0, 0, np, -1);
         } else {
-            const PairSlot ps = a.B == 1 ? PairSlot{lane, lane, 1, lane < np} : pair_slot(e, np, lane);
+            const PairSlot ps = a.B == 1 ? PairSlot{lane, lane, 1, lane < np} : pair_slot(e, np, lane, s_ps);
             if (lane < np) s_tok[ps.pos] = lane / a.k;
             if (ps.lead) {
                 s_act_e[ps.apos] = e;

@@ -27,6 +27,7 @@ template <int TB, int NS, int LPR, int NQ, int RP>
 __global__ __launch_bounds__(256) void layer_kernel(LayerArgs L) {
     extern __shared__ __align__(16) unsigned char s_dyn[];  // x staging, then h rows of down tasks
     __shared__ int32_t s_pair_e[4 * kMaxTopK];
+    __shared__ __align__(16) int32_t s_ps[128];  // pair_slot scratch
 
     __shared__ float s_acc[4 * DownShape<LPR, NQ, RP>::R];  // batch <= 4
     __shared__ int s_task, s_flag;
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(256) void layer_kernel(LayerArgs L) {
             router_rows<TB, true>(a, t, s_x);
             if (arrive_last(reinterpret_cast<unsigned*>(&meta[M_ROUTER_CNT]), L.n_router, &s_flag)) {
                 select_tokens<NS>(a, 0, a.z, nullptr, false, s_pair_e);
-                if ((tid >> 6) == 0) bucket_wave(a, s_pair_e, tid & 63);
+                if ((tid >> 6) == 0) bucket_wave(a, s_pair_e, tid & 63, s_ps);
                 publish(&meta[M_SEL]);
             }
         } else if (t < t_sdown) {
