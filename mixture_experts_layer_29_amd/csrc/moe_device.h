@@ -374,30 +374,32 @@ __device__ __forceinline__ void bucket_meta(const RouterArgs& a, int nact, int n
     st_dev(a.meta + M_ROUTER_CNT, 0);  // re-armed for the next launch
 }
 
-// Slot of pair `lane` (expert e) among np <= 64 pairs held one per lane: the
-// number of pairs with a smaller (expert, pair) key, so slots are ordered by
-// expert then token.  The first pair of each expert leads; entries (active
-// experts) are numbered in expert order (apos) and an entry's slots start at
-// its lead's slot; cnt (set for leads) is the expert's pair count.
+// Slot of pair `lane` (expert e) among np <= 64 pairs held one per lane.
+// Entries (active experts) come in two classes, experts with at least
+// mfma_min pairs ("hot", only when mfma_min > 0) first, then the rest, each by
+// ascending id; an entry's slots follow in the same order, by token inside an
+// entry.  pos: the pair's slot; the first pair of each expert leads; apos:
+// the entry's position (set for leads); cnt: the expert's pair count; hot: its
+// class.
 //
 // Runs in one wave with 128 ints of LDS (s_ps) of its own: every lane writes
-// its unique key (expert * 64 + lane) to LDS and counts the smaller keys from
-// broadcast reads of all of them (a rank, so the keys' sorted positions), then
-// scatters its key to its sorted position; neighbours in sorted order give the
-// leads, a ballot of the leads gives apos and cnt.  LDS accesses of one wave
-// complete in issue order, so the compiler-only fences are all the ordering
-// this needs.  (A loop of per-lane readlanes instead cost ~5 us for 64 pairs.)
+// its unique key (class, expert, lane) to LDS and counts the smaller keys from
+// broadcast reads of all of them (a rank, i.e. the key's sorted position),
+// then scatters its key to that position; neighbours in sorted order give the
+// leads, and a ballot of the leads gives apos and the counts.  The class needs
+// the counts, so a second pass ranks again when any expert is hot.  LDS
+// accesses of one wave complete in issue order, so compiler-only fences are
+// all the ordering this needs.  (A loop of per-lane readlanes cost ~5 us for
+// 64 pairs.)
 struct PairSlot {
     int pos, apos, cnt;
-    bool lead;
+    bool lead, hot;
 };
-__device__ __forceinline__ PairSlot pair_slot(int e, int np, int lane, int32_t* s_ps) {
-    constexpr int kPad = 1 << 20;  // above every expert id (E <= 1024)
-    const bool act = lane < np;
-    const int key = (act ? e : kPad) * 64 + lane;
+__device__ __forceinline__ void rank_pass(int key, bool act, int np, int lane, int32_t* s_ps, int& pos,
+                                          unsigned long long& lm) {
     s_ps[lane] = key;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    int pos = 0;
+    pos = 0;
     const int4* k4 = reinterpret_cast<const int4*>(s_ps);
     const int nq = (np + 15) >> 4;
     for (int q = 0; q < nq; ++q) {
@@ -412,14 +414,33 @@ __device__ __forceinline__ PairSlot pair_slot(int e, int np, int lane, int32_t* 
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const int cur = act ? s_ps[64 + lane] >> 6 : -1;
     const int prev = (act && lane > 0) ? s_ps[63 + lane] >> 6 : -1;
-    const unsigned long long lm = __ballot(act && cur != prev);  // leads, by sorted position
-    PairSlot r{0, 0, 0, false};
+    lm = __ballot(act && cur != prev);  // leads, by sorted position
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ PairSlot pair_slot(int e, int np, int lane, int32_t* s_ps, int mfma_min = 0) {
+    constexpr int kPad = 1 << 21;  // inactive lanes: above every class and expert id (E <= 1024)
+    const bool act = lane < np;
+    int key = (act ? e : kPad) * 64 + lane, pos;
+    unsigned long long lm;
+    rank_pass(key, act, np, lane, s_ps, pos, lm);
+    const int p = act ? pos : 0;
+    // the pair's expert's count: from its lead (highest lead at or below p) to the next lead
+    const unsigned long long below = lm & ((p < 63 ? (2ull << p) : 0ull) - 1ull);
+    const unsigned long long above = p < 63 ? (lm >> (p + 1)) << (p + 1) : 0ull;
+    const int lead_at = 63 - __clzll(below | 1ull);
+    const int cnt = (above ? __ffsll(above) - 1 : np) - lead_at;
+    const bool hot = act && mfma_min > 0 && cnt >= mfma_min;
+    if (__ballot(hot)) {  // second pass: hot experts' keys first
+        key = (act && !hot ? (1 << 26) : 0) + key;
+        rank_pass(key, act, np, lane, s_ps, pos, lm);
+    }
+    PairSlot r{0, 0, 0, false, false};
     if (act) {
         r.pos = pos;
         r.lead = (lm >> pos) & 1ull;
         r.apos = __popcll(lm & ((1ull << pos) - 1ull));
-        const unsigned long long above = pos < 63 ? (lm >> (pos + 1)) << (pos + 1) : 0ull;
-        r.cnt = (above ? __ffsll(above) - 1 : np) - pos;
+        r.cnt = cnt;
+        r.hot = hot;
     }
     return r;
 }
@@ -433,14 +454,14 @@ __device__ __forceinline__ void bucket_wave(const RouterArgs& a, const int32_t* 
         if (lane == 0) bucket_meta(a, 0, 0, np, -1);
         return;
     }
-    const PairSlot ps = pair_slot(e, np, lane, s_ps);
+    const PairSlot ps = pair_slot(e, np, lane, s_ps, a.mfma_min_tokens);
     if (lane < np) st_dev(a.perm + ps.pos, lane);
     if (ps.lead) {
         st_dev(a.act_e + ps.apos, e);
         st_dev(a.act_off + ps.apos, ps.pos);
     }
     const int nact = __popcll(__ballot(ps.lead));
-    const int nmfma = __popcll(__ballot(ps.lead && a.mfma_min_tokens > 0 && ps.cnt >= a.mfma_min_tokens));
+    const int nmfma = __popcll(__ballot(ps.lead && ps.hot));
     if (lane == 0) bucket_meta(a, nact, nmfma, np, np);
 }
 

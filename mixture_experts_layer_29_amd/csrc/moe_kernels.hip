@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void topk_bucket_kernel(TopkArgs ta) {
         for (int p = tid; p < np; p += 256) s_pair_e[p] = ld_dev(a.topk_idx + p);
         __syncthreads();
     }
-    if (np <= 32) {
+    if (np <= 64) {
         if (wave == 0) bucket_wave(a, s_pair_e, lane, s_ps);
     } else {
         bucket_block(a, s_pair_e, s_rank, s_cnt, s_tmp, &s_nmfma);
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
         if (__ballot(lane < np && (e < 0 || e >= a.E))) {  // never hand an invalid id to the experts
             if (out && lane == 0) bucket_meta(a, 0, 0, np, -1);
         } else {
-            const PairSlot ps = a.B == 1 ? PairSlot{lane, lane, 1, lane < np} : pair_slot(e, np, lane, s_ps);
+            const PairSlot ps = a.B == 1 ? PairSlot{lane, lane, 1, lane < np, false} : pair_slot(e, np, lane, s_ps);
             if (lane < np) s_tok[ps.pos] = lane / a.k;
             if (ps.lead) {
                 s_act_e[ps.apos] = e;
