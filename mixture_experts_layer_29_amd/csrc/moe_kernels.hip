@@ -566,7 +566,7 @@ __global__ __launch_bounds__(256) void down_os_kernel(DownArgs a) {
             d = dot8_hilo(w[q], *reinterpret_cast<const u32x4*>(s_hh + pe),
                           *reinterpret_cast<const u32x4*>(s_hl + pe), d);
         }
-        return group_sum<LPR>(d);
+        return d;  // this lane's part; the row's LPR lanes are summed once per token at the end
     };
     auto add = [&](int t, float v) {
 #pragma unroll
@@ -597,6 +597,8 @@ __global__ __launch_bounds__(256) void down_os_kernel(DownArgs a) {
         process(c0 + CE, wb1);
         if (c0 + 3 * CE < total) load_later(c0 + 3 * CE, wb1);
     }
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] = group_sum<LPR>(acc[t]);
     if (c == 0) {
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
