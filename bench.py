@@ -57,7 +57,7 @@ METRIC = "MoE decode layer µs & tokens/s at batch 1/16/64; achieved HBM GB/s vs
 # WRITE_SIZE x 1.0 KiB per dispatch, the scales a 2 GiB device copy gives
 # those counters), taken on the kernel sources with these SHA-1s and reported
 # only while the sources are unchanged (profiles/layer_tp8shard_b1_hbm_traffic.md).
-B1_TRAFFIC = {"kernels": {"front": (6360.7, 28.0), "experts_b1": (45036.7, 112.2)},
+B1_TRAFFIC = {"kernels": {"front": (6360.7, 28.0), "experts": (45036.7, 112.2)},
               "fetch_scale": 2.0, "write_scale": 1.0,
               "sources": {'moe_fused.hip': '3cb4841998349b1a913f896a54b38572c9df49bd', 'moe_kernels.hip': 'b4ab2d098ae53118dc94e4dda2726bea0164235b', 'moe_device.h': 'a68d097bde31ec7214ddf8816a5abe073a9e7b21', 'moe_args.h': '91e31570da8b9bd650ae48c274f51ffded8e0cb9'}}
 
@@ -506,7 +506,7 @@ def main():
         + 2 * wl.hidden * wl.shared_inter,
         # batch 1, one launch after the router launch: routed gate/up and down
         # rows and the shared expert's down rows
-        "experts_b1": float(sum(2 * 3 * wl.hidden * wl.inter * int(u) for u in nu1)) / len(nu1)
+        "experts": float(sum(2 * 3 * wl.hidden * wl.inter * int(u) for u in nu1)) / len(nu1)
         + 2 * wl.hidden * wl.shared_inter,
         "layer": head["weight_bytes_mean"],
     }.get(dom)

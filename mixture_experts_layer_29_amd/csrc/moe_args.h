@@ -152,7 +152,7 @@ struct FrontArgs {
     // of `dsteps` 32-wide steps; router partials to r.zacc, shared gate/up
     // partials [dks][B][2 Is] to `spart`
     float* spart;
-    int32_t* sync_clear;    // words zeroed by workgroup 0 (the batch-1 fused launch's sync block) or null
+    int32_t* sync_clear;    // words zeroed by workgroup 0 (the fused experts launch's sync block) or null
     int32_t sync_words;
     int32_t dks, dsteps;
     int32_t dks_r, dsteps_r;  // the router tiles' K splits and steps (fewer partials for the top-k launch)
@@ -200,45 +200,48 @@ struct LayerArgs {
     int32_t shared_mfma;    // shared expert on MFMA tiles
 };
 
-// Batch 1 in two launches: front_split_kernel (router logits z and the
+// Batch 1 and 2 in two launches: front_split_kernel (router logits z and the
 // shared expert's h, one row / row pair per workgroup; it also clears the
-// sync block below) and fused_b1_kernel, one grid of co-resident workgroups
-// (the host sizes it from the occupancy):
-//   select    every workgroup selects the top-k from z itself (no hand-off);
-//   gate/up   workgroup b computes routed tile b: four row pairs (one per wave)
-//             of selected expert j = b / (I/4), stores its h_j rows and counts
-//             them on expert j's own counter; the tile that completes expert j
-//             raises j's flag in every replica of the flag block;
-//   down      workgroup b owns output rows [b*R, b*R + R).  Right after the
-//             selection it requests its W2 rows of the k selected experts and
-//             its S2 rows (static weights: they stream with the gate/up rows),
-//             then accumulates each expert as soon as that expert's flag is up
-//             (per-expert readiness), in a fixed order, adds the shared expert
-//             and the residual and writes the row in bf16.
+// counters of the sync block below) and fused_experts_kernel, one grid of
+// co-resident workgroups (the host sizes it from the occupancy):
+//   select    waves t < B of every workgroup select token t's top-k from z
+//             (no hand-off);
+//   gate/up   the B k (token, expert) pairs are the units; workgroup b
+//             computes tiles b, b + G, ... (four row pairs each, one per
+//             wave), stores their h rows, then counts each tile on its pair's
+//             counter; the tile that completes pair p raises p's flag in every
+//             replica of the flag block;
+//   down      workgroup b owns output rows [b*R, b*R + R): it requests its W2
+//             rows of the B k pairs once its h is counted (its S2 rows before
+//             the selection), accumulates each pair as soon as that pair's
+//             flag is up (per-pair readiness), in a fixed order per token,
+//             adds the shared expert and the residual and writes the rows in
+//             bf16.
 // Sync block (int32 words, each counter and flag replica on its own 256-byte
-// line): counter of expert j at word 64 j; flag replica r at word
-// 64 (kMaxTopK + r), flag of expert j its word j.
+// line): counter of pair p at word 64 p; flag replica r at word
+// 64 (kMaxFusedPairs + r), flag of pair p its word p.
 constexpr int kSyncLineWords = 64;
 constexpr int kFlagReplicas = 16;
-constexpr int kSyncWords = (kMaxTopK + kFlagReplicas) * kSyncLineWords;
+constexpr int kMaxFusedPairs = 32;
+constexpr int kSyncWords = (kMaxFusedPairs + kFlagReplicas) * kSyncLineWords;
 struct FusedArgs {
-    const uint16_t* x;       // bf16 [H] (batch 1)
-    const float* z;          // fp32 [E] logits (bias included), from the front launch
-    const float* hs;         // fp32 [Is] shared h, from the front launch
+    const uint16_t* x;       // bf16 [B][H]
+    const float* z;          // fp32 [B][E] logits (bias included), from the front launch
+    const float* hs;         // fp32 [B][Is] shared h, from the front launch
     const uint16_t* w13;     // bf16 [E][2I][H]
     const uint16_t* w2;      // bf16 [E][H][I]
     const uint16_t* s2;      // bf16 [H][Is] or null
-    uint16_t* out;           // bf16 [H]
-    float* h;                // fp32 [k][I] routed h, by selection rank
-    int32_t* sync;           // [kSyncWords], zero at launch (cleared by the front launch)
+    uint16_t* out;           // bf16 [B][H]
+    float* h;                // fp32 [B k][I] routed h, by pair (token-major, selection rank)
+    int32_t* sync;           // [kSyncWords], counters zero at launch (cleared by the front launch)
     // routing results for the caller (written by workgroup 0)
-    int32_t* topk_idx;       // [k]
-    float* topk_w;           // [k]
+    int32_t* topk_idx;       // [B][k]
+    float* topk_w;           // [B][k]
     int32_t* meta;
     int32_t* act_e;
     int32_t* act_off;
     int32_t* perm;
-    int32_t H, E, k, I, Is;
+    int32_t H, E, k, I, Is, B;
     int32_t score_fn, renormalize;
     float routed_scale;
     int32_t add_residual;
@@ -250,9 +253,9 @@ struct FusedArgs {
     const uint16_t* pf_b;    // the next layer's shared expert weights
     long long pf_b_units;
 };
-constexpr int kPrefetchUnits = 16;  // 16-byte prefetch loads per lane (waves 1-3 of each workgroup)
+constexpr int kPrefetchUnits = 16;  // 16-byte prefetch loads per lane (the non-selecting waves)
 constexpr int kFusedRowThreads = 16;   // threads per output row in the down phase
-constexpr int kFusedMaxUnits = 16;     // W2 16-byte units per thread
+constexpr int kFusedMaxUnits = 32;     // W2 16-byte units per thread
 constexpr int kFusedMaxSUnits = 4;     // S2 16-byte units per thread
 
 // Writes the shared expert's constant work list (once per workspace, or before
@@ -282,7 +285,7 @@ KernelPick pick_init(const InitArgs& a);
 // Launch shape of the batch-1 single launch for this shape (grid = the
 // workgroups it needs), given how many of its workgroups fit on the device at
 // once; func is null where it does not apply or does not fit.
-KernelPick pick_fused_b1(const FusedArgs& a, int resident_wgs);
+KernelPick pick_fused_experts(const FusedArgs& a, int resident_wgs);
 
 // Device scratch of the allocation-free forward: a static array, one copy per
 // GPU, held until the process ends (moe_scratch.hip).

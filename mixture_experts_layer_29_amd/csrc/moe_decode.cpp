@@ -70,7 +70,7 @@ constexpr int kDownOsMaxBatch = 4;        // output-stationary down up to this b
 enum Slot { S_FRONT = 0, S_TOPK = 1, S_GATEUP = 2, S_SHARED = 3, S_DOWN = 4, S_LAYER = 5, S_COMBINE = 6,
             S_EXPERTS = 7, S_COUNT = 8 };
 const char* kSlotNames[S_COUNT] = {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine",
-                                   "layer", "combine", "experts_b1"};
+                                   "layer", "combine", "experts"};
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -115,7 +115,7 @@ struct moe_decode_plan_s {
     bool select_in_gateup;// batch <= 4: every routed gate/up workgroup selects and buckets
     bool shared_in_gateup;// that form also runs the shared gate/up row pairs (one per workgroup)
     bool fused;           // the whole layer as one persistent launch (batch <= 4, on request)
-    bool fused_b1;        // batch 1: the whole layer as one launch (fused_b1_kernel)
+    bool fused_small;     // batch 1-2: router launch + one fused experts launch (fused_experts_kernel)
     int fb_grid = 0;      // its workgroups on this device (0 until resolved)
     int sel_grid = 0;     // select-in-gate/up form: workgroups the device holds at once (0 until known)
     bool expert_major;    // staged down: expert-major tiles + combine launch (else output-stationary)
@@ -164,29 +164,35 @@ bool topk_own_launch(const moe_decode_plan_s* p) { return !p->select_in_router &
 bool shared_in_front(const moe_decode_plan_s* p) { return has_shared(p) && !p->shared_stream; }
 
 
-// The batch-1 single launch needs all of its workgroups resident at once: its
-// grid against what the occupancy allows on the current device.  Falls back
-// to the staged launches (fused_b1 = false) where they do not fit.
-moe_status resolve_fused_b1(moe_decode_plan_s* p) {
-    if (!p->fused_b1 || p->fb_grid) return MOE_OK;
-    const moe_decode_config& c = p->cfg;
+// The fused experts launch (batch 1-2) needs all of its workgroups resident at
+// once: its grid, sized from what the occupancy allows on the current device.
+// Falls back to the staged launches (fused_small = false) where it does not fit.
+FusedArgs fused_shape(const moe_decode_config& c) {
     FusedArgs f{};
     f.H = c.hidden;
     f.E = c.n_experts;
     f.k = c.top_k;
     f.I = c.inter;
     f.Is = c.shared_inter;
-    const KernelPick k = pick_fused_b1(f, 1 << 30);
+    f.B = c.batch;
+    return f;
+}
+
+moe_status resolve_fused_small(moe_decode_plan_s* p) {
+    if (!p->fused_small || p->fb_grid) return MOE_OK;
+    const FusedArgs f = fused_shape(p->cfg);
+    KernelPick k = pick_fused_experts(f, 1 << 30);
     if (!k.func) {
-        p->fused_b1 = false;
+        p->fused_small = false;
         return MOE_OK;
     }
     int dev = 0, per_cu = 0, cus = 0;
     HIP_TRY(hipGetDevice(&dev));
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.func, 256, 0));
     HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-    if ((long long)per_cu * cus < (long long)k.grid.x) {
-        p->fused_b1 = false;
+    k = pick_fused_experts(f, per_cu * cus);
+    if (!k.func) {
+        p->fused_small = false;
         return MOE_OK;
     }
     p->fb_grid = (int)k.grid.x;
@@ -398,6 +404,7 @@ void fill_static_args(moe_decode_plan_s* p, char* ws, Launches& A, bool clear) {
         f.k = c.top_k;
         f.I = c.inter;
         f.Is = c.shared_inter;
+        f.B = c.batch;
         f.score_fn = c.score_fn;
         f.renormalize = c.renormalize;
         f.routed_scale = c.routed_scale;
@@ -483,7 +490,7 @@ void set_pointers(moe_decode_plan_s* p, Launches& A, const void* x, const void* 
     A.dx.w2 = A.da.w2;
     A.dx.s2 = A.da.s2;
     A.dx.out = A.da.out;
-    if (p->fused_b1) {
+    if (p->fused_small) {
         FusedArgs& f = A.fb;
         f.x = xb;
         f.w13 = ew;
@@ -494,7 +501,7 @@ void set_pointers(moe_decode_plan_s* p, Launches& A, const void* x, const void* 
         f.pf_a_units = next_router_w ? (long long)c.n_experts * c.hidden / 8 : 0;
         f.pf_b = has_shared(p) ? static_cast<const uint16_t*>(next_shared_w) : nullptr;
         f.pf_b_units = f.pf_b ? 3LL * c.shared_inter * c.hidden / 8 : 0;
-        A.kb = pick_fused_b1(f, p->fb_grid);
+        A.kb = pick_fused_experts(f, p->fb_grid);
         // its router launch: one router row per workgroup, then one shared
         // gate/up row pair per workgroup; workgroup 0 re-arms the sync block
         A.fbf = A.fa;
@@ -589,7 +596,7 @@ moe_status device_init_once(moe_decode_plan_s* p, hipStream_t stream, int dev) {
     // zero once: counters re-arm themselves and split-K partials are cleared after use
     HIP_TRY(hipMemsetAsync(p->ws, 0, p->L.total, stream));
     Launches& A = p->m;
-    moe_status st = resolve_fused_b1(p);
+    moe_status st = resolve_fused_small(p);
     if (st) return st;
     fill_static_args(p, p->ws, A, false);
     {
@@ -627,7 +634,7 @@ moe_status launch(const KernelPick& k, void* args, hipStream_t s) {
 // second stream).  ev: per-slot start/end events for timing, or null.
 moe_status enqueue_eager(moe_decode_plan_s* p, Launches& A, hipStream_t stream, hipEvent_t* ev) {
     moe_status st;
-    if (p->fused_b1) {
+    if (p->fused_small) {
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT], stream));
         if ((st = launch(A.kbf, &A.fbf, stream))) return st;
         if (ev) HIP_TRY(hipEventRecord(ev[2 * S_FRONT + 1], stream));
@@ -688,7 +695,7 @@ hipKernelNodeParams node_params(const KernelPick& k, void** args) {
 moe_status build_graph(moe_decode_plan_s* p) {
     Launches& A = p->m;
     HIP_TRY(hipGraphCreate(&p->graph, 0));
-    if (p->fused_b1) {
+    if (p->fused_small) {
         void* af[] = {&A.fbf};
         void* ae[] = {&A.fb};
         hipKernelNodeParams np = node_params(A.kbf, af);
@@ -740,7 +747,7 @@ moe_status build_graph(moe_decode_plan_s* p) {
 
 moe_status patch_graph(moe_decode_plan_s* p) {
     Launches& A = p->m;
-    if (p->fused_b1) {
+    if (p->fused_small) {
         void* af[] = {&A.fbf};
         void* ae[] = {&A.fb};
         hipKernelNodeParams np = node_params(A.kbf, af);
@@ -927,21 +934,14 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
     p->shared_in_gateup = p->select_in_gateup && shared_in_front(p) &&
                           (size_t)c.shared_inter <= std::min((size_t)p->max_act * (c.inter / kPairsPerGemvTile),
                                                              kSelectGateupMaxTiles);
-    // Batch 1: the whole layer as one launch where the shape has a batch-1
-    // kernel (GEMV tiles only: no MFMA threshold the batch reaches), unless
-    // the caller asks for another form.  Whether its grid fits the device is
-    // checked at the first forward (else the staged launches run).
-    {
-        FusedArgs f{};
-        f.H = c.hidden;
-        f.E = c.n_experts;
-        f.k = c.top_k;
-        f.I = c.inter;
-        f.Is = c.shared_inter;
-        p->fused_b1 = c.batch == 1 && !p->fused && c.single_launch == 0 && !p->shared_stream &&
-                      c.topk_launch == 0 && !p->shared_mfma && (p->mfma_min == 0 || p->mfma_min > 1) &&
-                      pick_fused_b1(f, 1 << 30).func != nullptr;
-    }
+    // Batch 1-2: the router launch and one fused experts launch where the
+    // shape has such a kernel (GEMV tiles only: no MFMA threshold the batch
+    // reaches), unless the caller asks for another form.  Whether its grid
+    // fits the device is checked at the first forward (else the staged
+    // launches run).
+    p->fused_small = c.batch <= 2 && !p->fused && c.single_launch == 0 && !p->shared_stream && c.topk_launch == 0 &&
+                  !p->shared_mfma && (p->mfma_min == 0 || p->mfma_min > c.batch) &&
+                  pick_fused_experts(fused_shape(c), 1 << 30).func != nullptr;
     p->expert_major = c.batch > kDownOsMaxBatch;
     p->L = make_layout(c, p->max_act, p->variant == MOE_VARIANT_SPLIT_K, p->fused, p->expert_major,
                        p->small_router ? 1 : p->dks_r,
@@ -1022,7 +1022,7 @@ moe_status moe_decode_forward_noalloc(moe_decode_plan_t p, const void* x, const 
     if (has_shared(p) && p->shared_stream)
         return fail(MOE_ERR_UNSUPPORTED, "the allocation-free forward runs on the caller's stream only; this "
                     "plan puts the shared expert on a second stream (shared_stream = 1)");
-    if ((st = resolve_fused_b1(p))) return st;
+    if ((st = resolve_fused_small(p))) return st;
     void* scratch = nullptr;
     size_t scratch_bytes = 0;
     HIP_TRY(scratch_for_current_device(&scratch, &scratch_bytes));
@@ -1093,18 +1093,18 @@ moe_status moe_decode_plan_info(moe_decode_plan_t p, moe_decode_info* info) {
     g_err.clear();
     if (!p || !info) return fail(MOE_ERR_INVALID, "NULL argument");
     info->variant = p->variant;
-    info->n_kernels = p->fused ? 1 : p->fused_b1 ? 2
+    info->n_kernels = p->fused ? 1 : p->fused_small ? 2
                       : 3 + (topk_own_launch(p) ? 1 : 0) + (has_shared(p) && p->shared_stream ? 1 : 0) +
                             (p->expert_major ? 1 : 0);
-    info->topk_launch = p->fused || p->fused_b1 ? 0 : p->select_in_gateup ? 3 : p->select_in_router ? 1 : 2;
+    info->topk_launch = p->fused || p->fused_small ? 0 : p->select_in_gateup ? 3 : p->select_in_router ? 1 : 2;
     info->mfma_min_tokens = p->mfma_min;
     info->shared_mfma = p->shared_mfma ? 1 : 0;
     info->shared_stream = p->shared_stream ? 1 : 0;
     info->router_mfma = p->small_router ? 0 : 1;
-    info->single_launch = p->fused ? 1 : p->fused_b1 ? 2 : 0;
-    info->layer_grid = p->fused_b1 ? p->fb_grid : p->layer_grid;
+    info->single_launch = p->fused ? 1 : p->fused_small ? 2 : 0;
+    info->layer_grid = p->fused_small ? p->fb_grid : p->layer_grid;
     info->workspace_bytes = p->L.total;
-    info->shared_gateup_in = !has_shared(p) ? 0 : p->fused ? 4 : p->fused_b1 ? 1 : p->shared_stream ? 3
+    info->shared_gateup_in = !has_shared(p) ? 0 : p->fused ? 4 : p->fused_small ? 1 : p->shared_stream ? 3
                              : p->shared_in_gateup ? 2 : 1;
     return MOE_OK;
 }
@@ -1136,7 +1136,7 @@ moe_status moe_decode_profile_read(moe_decode_plan_t p, int32_t cap, double* tot
     if (p->prof_count == 0) return MOE_OK;
     for (int f = 0; f < p->prof_count; ++f) {
         for (int s = 0; s < S_COUNT && s < cap; ++s) {
-            const bool used = p->fused_b1 ? (s == S_FRONT || s == S_EXPERTS)
+            const bool used = p->fused_small ? (s == S_FRONT || s == S_EXPERTS)
                               : p->fused ? s == S_LAYER
                               : !((s == S_SHARED && !(has_shared(p) && p->shared_stream)) ||
                                   (s == S_TOPK && !topk_own_launch(p)) || s == S_LAYER || s == S_EXPERTS ||

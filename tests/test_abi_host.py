@@ -127,18 +127,17 @@ def test_auto_variant(batch, variant):
     p = moe.Plan(cfg(batch=batch))
     info = p.info()
     assert info.variant == variant
-    # batch 1: router, gate/up (selecting for itself, shared gate/up
-    # included), down -- its gate/up grid (8 experts x 64 tiles) is one
-    # generation of workgroups; batch 2-4: router (+ selection in its last
-    # workgroup, + shared gate/up), gate/up, down; above: router MFMA launch
+    # batch 1-2: router (+ shared gate/up), then the fused experts launch
+    # (grid checked at the first forward); batch 3-4: router (+ shared
+    # gate/up), gate/up selecting for itself, down; above: router MFMA launch
     # (+ shared gate/up), top-k launch, routed gate/up, expert-major down,
     # combine
     big = 1 if batch > 4 else 0
-    one = batch == 1  # batch 1: the whole layer as one launch (grid checked at the first forward)
+    one = batch <= 2  # the router launch and one fused experts launch
     assert info.router_mfma == big
     assert info.single_launch == (2 if one else 0)
     assert info.n_kernels == (2 if one else 3 + 2 * big)
-    # batch 2-4: every gate/up workgroup selects for itself (a grid of at most
+    # batch 3-4: every gate/up workgroup selects for itself (a grid of at most
     # one generation, looping over the tiles), the shared expert's row pairs
     # in the first gate/up workgroups; above: a top-k launch
     assert info.topk_launch == (0 if one else 2 if big else 3)
@@ -161,7 +160,7 @@ def test_auto_variant(batch, variant):
     p.destroy()
     p = moe.Plan(cfg(batch=batch, single_launch=moe.SINGLE_OFF))
     assert p.info().n_kernels == 3 + 2 * big and p.info().single_launch == 0
-    if one:  # the staged form at batch 1: every gate/up workgroup selects for itself
+    if one:  # the staged form at batch 1-2: every gate/up workgroup selects for itself
         assert p.info().topk_launch == 3 and p.info().shared_gateup_in == 2
     p.destroy()
     if batch <= 4:
@@ -276,7 +275,7 @@ def test_profiling_toggle_without_device():
     p.set_profiling(True)
     prof = p.profile_read()
     assert set(prof) == {"front", "topk_bucket", "gateup_routed", "gateup_shared", "down_combine", "layer",
-                         "combine", "experts_b1"}
+                         "combine", "experts"}
     assert all(v == (0.0, 0) for v in prof.values())
     p.set_profiling(False)
     p.destroy()

@@ -83,10 +83,10 @@ def test_tp8_uniform(tp8, batch):
     shape = shape_of(synthetic.TP8)
     m, st, info = check(tp8, shape, batch, "tp8 B=%d" % batch)
     assert info.variant == (moe.VARIANT_SMALL_M if batch <= 2 else moe.VARIANT_SPLIT_K)
-    # batch 1: the router launch, then the routed experts, shared down and
+    # batch 1-2: the router launch, then the routed experts, shared down and
     # combine in one launch over a grid of 512 resident workgroups
-    assert info.single_launch == (2 if batch == 1 else 0)
-    if batch == 1:
+    assert info.single_launch == (2 if batch <= 2 else 0)
+    if batch <= 2:
         assert info.n_kernels == 2 and info.layer_grid == 512
 
 
@@ -141,21 +141,22 @@ def test_tp8_single_launch_variants(tp8, batch, kw):
         assert st.mfma_tiles > 0 and st.gemv_tiles == 0
 
 
+@pytest.mark.parametrize("batch", [1, 2])
 @pytest.mark.parametrize("wl_name", ["tp8", "tiny"])
-def test_batch1_single_launch_agrees_with_staged_many_forwards(tp8, tiny, wl_name):
-    """Batch 1: the one-launch form against the staged launches over many
-    forwards with fresh inputs on one plan each.  Both are deterministic (GEMV
-    tiles, fixed summation orders), so each must repeat itself bit for bit,
-    and they differ only by fp32 summation order.  A counter that did not
+def test_batch1_single_launch_agrees_with_staged_many_forwards(tp8, tiny, wl_name, batch):
+    """Batch 1-2: the fused experts launch against the staged launches over
+    many forwards with fresh inputs on one plan each.  Both are deterministic
+    (GEMV tiles, fixed summation orders), so each must repeat itself bit for
+    bit, and they differ only by fp32 summation order.  A counter that did not
     re-arm, or a hand-off that read a previous forward's logits or h, breaks
     one of the checks."""
     layer = tp8 if wl_name == "tp8" else tiny
     shape = shape_of(layer.wl)
-    one = make_plan(layer, shape, 1)
-    staged = make_plan(layer, shape, 1, single_launch=moe.SINGLE_OFF)
-    g = torch.Generator().manual_seed(4321)
+    one = make_plan(layer, shape, batch)
+    staged = make_plan(layer, shape, batch, single_launch=moe.SINGLE_OFF)
+    g = torch.Generator().manual_seed(4321 + batch)
     for it in range(40):
-        x = (torch.randn(1, shape.hidden, generator=g) * (1 + it % 3)).to(torch.bfloat16).cuda()
+        x = (torch.randn(batch, shape.hidden, generator=g) * (1 + it % 3)).to(torch.bfloat16).cuda()
         o1, o2, o3 = (torch.empty_like(x) for _ in range(3))
         one.forward(x, layer.router_w, layer.expert_w, layer.shared_w, o1)
         one.forward(x, layer.router_w, layer.expert_w, layer.shared_w, o3)
@@ -373,7 +374,8 @@ def test_forwards_captured_into_a_caller_graph(tp8, batch, shared_stream):
 @pytest.mark.parametrize("B,kw,slots", [
     (16, {}, {"front", "topk_bucket", "gateup_routed", "down_combine", "combine"}),
     (1, dict(single_launch=moe.SINGLE_OFF), {"front", "gateup_routed", "down_combine"}),
-    (1, {}, {"front", "experts_b1"}),
+    (1, {}, {"front", "experts"}),
+    (2, {}, {"front", "experts"}),
 ])
 def test_profiling_path_matches(tp8, B, kw, slots):
     shape = shape_of(synthetic.TP8)
