@@ -89,10 +89,10 @@ typedef struct moe_decode_config {
                                 second queue); 1: on the plan's second stream,
                                 forked before the router and joined before the down
                                 projection                                           */
-    int32_t topk_launch;     /* batch <= 4 only.  0: default (3 where it applies
-                                and the routed gate/up grid is one generation of
-                                workgroups, at most 512 -- batch 1 of the TP8
-                                shape -- else 1); 1: top-k and bucketing in the router
+    int32_t topk_launch;     /* batch <= 4 only.  0: default (at batch 1-2 the
+                                fused experts launch where it applies, see
+                                single_launch; otherwise 3 where it applies, else
+                                1); 1: top-k and bucketing in the router
                                 launch's last workgroup to arrive; 2: in a launch of
                                 their own after the router; 3: in every routed
                                 gate/up workgroup, each deriving the same work lists
@@ -102,18 +102,18 @@ typedef struct moe_decode_config {
                                 default mfma_min_tokens that is what it does; a
                                 mfma_min_tokens <= batch keeps 0 at 1, and asking
                                 for 3 with it fails with MOE_ERR_UNSUPPORTED        */
-    int32_t single_launch;   /* 0 (default): the library's choice.  At batch 1, where
-                                the shape has a batch-1 experts kernel (H <= 8192,
-                                k * I <= 2048, Is a multiple of 128 up to 512) and
-                                the device holds its grid (k * I / 4 workgroups,
-                                two per CU: 512 at the TP8 shard) resident at once,
-                                two launches: the router (+ the shared expert's
-                                gate/up), then the routed experts, shared down and
-                                combine in ONE launch whose workgroups hand h over
-                                through per-expert counters (the Kimi K3 decode
-                                article, Part 1 section 2: producer and consumer
-                                fused at small batch); otherwise the staged
-                                launches.  1: the staged launches always.  2: the
+    int32_t single_launch;   /* 0 (default): the library's choice.  At batch 1-2,
+                                where the shape has a fused experts kernel (H <=
+                                8192, I a power of two from 128, batch * k * I <=
+                                4096, Is a multiple of 128 up to 512) and the device
+                                holds its grid (512 workgroups at the TP8 shard, two
+                                per CU) resident at once, two launches: the router
+                                (+ the shared expert's gate/up), then the routed
+                                experts, shared down and combine in ONE launch
+                                whose workgroups hand h over through per-(token,
+                                expert) counters (the Kimi K3 decode article, Part
+                                1 section 2: producer and consumer fused at small
+                                batch); otherwise the staged launches.  1: the staged launches always.  2: the
                                 whole layer as ONE persistent launch -- possible when
                                 batch <= 4, shared_stream = 0, topk_launch != 2 and
                                 the shape fits it (x and h staged in LDS), else
@@ -140,7 +140,7 @@ typedef struct moe_decode_info {
     int32_t shared_stream;    /* resolved shared_stream                                  */
     int32_t router_mfma;      /* 1: router is a split-K MFMA launch + a top-k launch     */
     int32_t single_launch;    /* 0: staged launches; 1: the layer runs as one persistent
-                                 launch (single_launch = 2 in the config); 2: batch 1
+                                 launch (single_launch = 2 in the config); 2: batch 1-2
                                  as router launch + one experts launch (before the
                                  first forward this assumes the device holds its
                                  grid; the first forward checks, else 0)           */
@@ -213,7 +213,7 @@ moe_status moe_decode_forward(moe_decode_plan_t plan, const void* x, const void*
  * decode article, Part 1 section 4 (prefetching future weights into the cache
  * from a phase that cannot use the memory bandwidth).  Either next pointer may
  * be NULL (nothing of it is prefetched); they are only read.  Issued by the
- * batch-1 experts launch (moe_decode_plan_info: single_launch = 2); the other
+ * batch 1-2 experts launch (moe_decode_plan_info: single_launch = 2); the other
  * launch forms ignore the next-layer pointers.  Errors as moe_decode_forward,
  * plus MOE_ERR_INVALID for a misaligned next pointer. */
 moe_status moe_decode_forward_prefetch(moe_decode_plan_t plan, const void* x, const void* router_w,
