@@ -2,27 +2,28 @@
 // staged form (one launch per stage; the single-launch form for batch <= 4
 // is in moe_layer.h).
 //
-// One layer is, on the main stream:
-//   front      batch 1: front_split -- one router row per workgroup, logits to
-//              z; the routed gate/up launch then selects in every workgroup
+// One layer is, on the main stream (batch 1-2: the router launch and the
+// fused experts launch of moe_fused.hip instead):
+//   front      batch 3-4: front_split -- one router row per workgroup, logits to
+//              z (and, where the gate/up launch has too few workgroups for
+//              them, the shared expert's gate/up row pairs); the routed gate/up
+//              launch then selects and buckets in every workgroup
 //              (gateup_select);
-//              batch 2-4: front_small -- router GEMV, then the last workgroup
-//              to arrive selects the top-k experts of every token, computes the
-//              routing weights and buckets the (token, slot) pairs by expert;
 //              batch > 4: front_dense -- dense split-K MFMA tiles writing plain
-//              fp32 partial logits (no atomics) -- then topk_bucket -- which
-//              sums the partials in a fixed order, selects with one wave per
-//              token, and buckets with an LDS histogram in its last workgroup;
-//              trailing workgroups of the front launch run the shared expert's
-//              gate/up, which needs only x;
+//              fp32 partial logits (no atomics) and the shared expert's gate/up
+//              partials -- then topk_bucket -- which sums the partials in a
+//              fixed order, selects with one wave per token, and buckets (one
+//              wave, or an LDS histogram) in its last workgroup;
 //   gateup     grouped gate/up projection + SiLU*up over the active experts:
 //              GEMV tiles (full K, VALU dot2) for experts with few tokens -- the
 //              "small-matrix" form the Kimi K3 decode article uses at batch 1-2
 //              -- and split-K MFMA tiles for experts with many tokens -- the
 //              "split-K" form it uses at larger batches (Part 1 section 1);
 //   down       down projection of every active expert and of the shared
-//              expert, routing-weighted sum, residual add, bf16 output;
-//              output-stationary, so no atomics and a fixed summation order;
+//              expert, routing-weighted sum, residual add, bf16 output: at
+//              batch 3-4 output-stationary (down_os: no atomics, fixed order);
+//              above, expert-major tiles with fp32 partial rows and a combine
+//              launch that sums them in a fixed order;
 // or, with shared_stream = 1, the shared expert's gate/up on a second stream
 // (same gateup kernel with a one-entry work list), joined before `down`
 // (article Part 1 section 3: the shared expert on its own stream, overlapped
