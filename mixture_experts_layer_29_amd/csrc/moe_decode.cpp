@@ -60,6 +60,7 @@ moe_status fail(moe_status st, const char* fmt, ...) {
 constexpr int kDefaultMfmaMin = 5;
 constexpr int kMaxProfiledForwards = 1024;
 constexpr int kSmallRouterMaxBatch = 4;
+constexpr int kTopkOneGroupMaxBatch = 8;     // the top-k launch selects in one workgroup up to this batch
 constexpr size_t kSelectGateupMaxTiles = 512;  // gate/up workgroups of one generation (2 per CU x 256 CUs)
 constexpr size_t kSmallRouterLds = 56 * 1024;
 
@@ -385,7 +386,10 @@ void fill_static_args(moe_decode_plan_s* p, char* ws, Launches& A, bool clear) {
     A.ta.hs = at<float>(ws, p->L.hs);
     A.ta.Is = c.shared_inter;
     A.ta.nspart = p->L.spart ? p->dks : 0;
-    A.ta.sel_blocks = (c.batch + 3) / 4;
+    // top-k launch: up to batch 8 (and 64 pairs, bucketed by one wave) one
+    // selecting workgroup with a wave per token (no hand-off between
+    // workgroups), else one workgroup per four tokens
+    A.ta.sel_blocks = c.batch <= kTopkOneGroupMaxBatch && c.batch * c.top_k <= 64 ? 1 : (c.batch + 3) / 4;
 
     {
         FusedArgs& f = A.fb;

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void front_dense_kernel(FrontArgs f) {
 // buckets all pairs.  Workgroups from sel_blocks on reduce the shared
 // expert's gate/up partials into h_s.
 template <int NS>
-__global__ __launch_bounds__(256) void topk_bucket_kernel(TopkArgs ta) {
+__global__ __launch_bounds__(512) void topk_bucket_kernel(TopkArgs ta) {
     __shared__ int32_t s_pair_e[kMaxBatch * kMaxTopK];
     __shared__ int32_t s_rank[kMaxBatch * kMaxTopK];
     __shared__ int32_t s_cnt[kMaxExperts];
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void topk_bucket_kernel(TopkArgs ta) {
     const RouterArgs& a = ta.r;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if ((int)blockIdx.x >= ta.sel_blocks) {
-        const int idx = (blockIdx.x - ta.sel_blocks) * 256 + tid;
+        const int idx = (blockIdx.x - ta.sel_blocks) * blockDim.x + tid;
         const int Is = ta.Is, n2 = 2 * Is;
         if (idx >= a.B * Is) return;
         const int t = idx / Is, i = idx - t * Is;
@@ -132,7 +132,9 @@ __global__ __launch_bounds__(256) void topk_bucket_kernel(TopkArgs ta) {
     }
     const int B = a.B, np = B * a.k;
     const bool single = ta.sel_blocks == 1;
-    select_tokens<NS, false>(a, blockIdx.x * 4, a.zacc, a.bias, true, single ? s_pair_e : nullptr);
+    // one selecting workgroup (blockDim / 64 >= B waves, one token each: no
+    // hand-off, no reload) or one per four tokens
+    select_tokens<NS, false>(a, single ? 0 : blockIdx.x * 4, a.zacc, a.bias, true, single ? s_pair_e : nullptr);
     if (!single) {
         if (!arrive_last(reinterpret_cast<unsigned*>(&a.meta[M_ROUTER_CNT]), ta.sel_blocks, &s_flag)) return;
         for (int p = tid; p < np; p += 256) s_pair_e[p] = ld_dev(a.topk_idx + p);
@@ -964,8 +966,11 @@ KernelPick pick_topk(const TopkArgs& t) {
         case 8: fn = MOE_FN(topk_bucket_kernel<8>); break;
         default: fn = MOE_FN(topk_bucket_kernel<16>); break;
     }
-    const int red = t.spart ? (a.B * t.Is + 255) / 256 : 0;
-    return {fn, dim3(t.sel_blocks + red), dim3(256), 0};
+    // one selecting workgroup of one wave per token up to batch 8, else
+    // 256-thread workgroups of four tokens each
+    const int threads = t.sel_blocks == 1 ? std::max(256, 64 * a.B) : 256;
+    const int red = t.spart ? (a.B * t.Is + threads - 1) / threads : 0;
+    return {fn, dim3(t.sel_blocks + red), dim3(threads), 0};
 }
 
 KernelPick pick_front_split(const FrontArgs& f) {
