@@ -872,6 +872,40 @@ __device__ __forceinline__ void gemv_gateup_tile(const GateUpArgs& a, const uint
     }
 }
 
+// Last of a row block's split-K tiles: h = SiLU(gate) * up for the block's
+// 64 row pairs and T tokens from the fp32 sums, which (with the block's
+// counter) it clears for the next step.  A thread requests the sums of
+// kFinishBatch elements at once: at 64 tokens it handles 16, and one at a
+// time would be 16 coherent round trips in a row.
+__device__ __forceinline__ void mfma_tile_finish(const GateUpArgs& a, int entry, int nrb, int rb, int off, int T) {
+    constexpr int kFinishBatch = 8;
+    const int tid = threadIdx.x, n = a.n, n2 = 2 * n;
+    const int rows = kPairsPerMfmaTile, total = rows * T;
+    for (int i0 = tid; i0 < total; i0 += 256 * kFinishBatch) {
+        float g[kFinishBatch], u[kFinishBatch];
+#pragma unroll
+        for (int q = 0; q < kFinishBatch; ++q) {
+            const int idx = min(i0 + 256 * q, total - 1);
+            const int j = idx / rows, i = rb * rows + idx % rows;
+            const float* gp = a.g_acc + (size_t)(off + j) * n2;
+            g[q] = ld_dev(gp + i);
+            u[q] = ld_dev(gp + n + i);
+        }
+#pragma unroll
+        for (int q = 0; q < kFinishBatch; ++q) {
+            const int idx = i0 + 256 * q;
+            if (idx < total) {
+                const int j = idx / rows, i = rb * rows + idx % rows;
+                float* gp = a.g_acc + (size_t)(off + j) * n2;
+                st_dev(a.h + (size_t)(off + j) * n + i, silu_f(g[q]) * u[q]);
+                st_dev(gp + i, 0.0f);
+                st_dev(gp + n + i, 0.0f);
+            }
+        }
+    }
+    if (tid == 0) st_dev(a.tile_cnt + entry * nrb + rb, 0u);
+}
+
 // Split-K MFMA tile: 64 row pairs (16 per wave) x one K slice x T <= 16*NTM
 // tokens (NTM 16-token column tiles; a small NTM keeps the register budget
 // small where the token count is known to be small).
@@ -947,16 +981,7 @@ __device__ __forceinline__ bool mfma_gateup_tile(const GateUpArgs& a, const uint
     }
     __shared__ int s_flag;
     if (!arrive_last(&a.tile_cnt[entry * nrb + rb], (unsigned)a.ksplit, &s_flag)) return true;
-    const int rows = kPairsPerMfmaTile;
-    for (int idx = tid; idx < rows * T; idx += 256) {
-        const int j = idx / rows, i = rb * rows + idx % rows;
-        float* gp = a.g_acc + (size_t)(off + j) * n2;
-        const float g = ld_dev(gp + i), u = ld_dev(gp + n + i);
-        st_dev(a.h + (size_t)(off + j) * n + i, silu_f(g) * u);
-        st_dev(gp + i, 0.0f);
-        st_dev(gp + n + i, 0.0f);
-    }
-    if (tid == 0) st_dev(a.tile_cnt + entry * nrb + rb, 0u);
+    mfma_tile_finish(a, entry, nrb, rb, off, T);
     return true;
 }
 
@@ -1055,16 +1080,7 @@ __device__ __forceinline__ bool mfma_gateup_tile_lds(const GateUpArgs& a, const 
     }
     __shared__ int s_flag;
     if (!arrive_last(&a.tile_cnt[entry * nrb + rb], (unsigned)a.ksplit, &s_flag)) return true;
-    const int rows = kPairsPerMfmaTile;
-    for (int idx = tid; idx < rows * T; idx += 256) {
-        const int j = idx / rows, i = rb * rows + idx % rows;
-        float* gp = a.g_acc + (size_t)(off + j) * n2;
-        const float g = ld_dev(gp + i), u = ld_dev(gp + n + i);
-        st_dev(a.h + (size_t)(off + j) * n + i, silu_f(g) * u);
-        st_dev(gp + i, 0.0f);
-        st_dev(gp + n + i, 0.0f);
-    }
-    if (tid == 0) st_dev(a.tile_cnt + entry * nrb + rb, 0u);
+    mfma_tile_finish(a, entry, nrb, rb, off, T);
     return true;
 }
 

@@ -703,22 +703,38 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
 
     uint32_t* s_hl = s_hh + (size_t)T * I / 2;
     // h rows to LDS as bf16 hi + lo pairs (when they fit) and the tokens'
-    // output row offsets; called once the band's first weights are requested
+    // output row offsets; called once the band's first weights are requested.
+    // A thread requests kStageBatch float4 of h at a time: a many-token tile
+    // stages up to 16 per thread, and one at a time would be as many L2 round
+    // trips in a row.
     auto stage = [&]() {
         if (tid < T) s_dsto[tid] = (routed ? a.perm[off_r + tid] : sblk * B + tid) * H;
         if (h_lds) {
-            const int I4 = I / 4;
-            for (int i = tid; i < T * I4; i += 256) {
-                const int j = i / I4, c4 = i - j * I4;
-                const float4 v = *reinterpret_cast<const float4*>(hsrc + (size_t)j * hstride + 4 * c4);
-                const uint32_t h0 = f32_to_bf16_rne(v.x), h1 = f32_to_bf16_rne(v.y);
-                const uint32_t h2 = f32_to_bf16_rne(v.z), h3 = f32_to_bf16_rne(v.w);
-                const uint32_t l0 = f32_to_bf16_rne(v.x - __uint_as_float(h0 << 16));
-                const uint32_t l1 = f32_to_bf16_rne(v.y - __uint_as_float(h1 << 16));
-                const uint32_t l2 = f32_to_bf16_rne(v.z - __uint_as_float(h2 << 16));
-                const uint32_t l3 = f32_to_bf16_rne(v.w - __uint_as_float(h3 << 16));
-                reinterpret_cast<uint2*>(s_hh)[i] = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
-                reinterpret_cast<uint2*>(s_hl)[i] = uint2{l0 | (l1 << 16), l2 | (l3 << 16)};
+            constexpr int kStageBatch = 2;
+            const int I4 = I / 4, n4 = T * I4;
+            for (int i0 = tid; i0 < n4; i0 += 256 * kStageBatch) {
+                float4 v[kStageBatch];
+#pragma unroll
+                for (int q = 0; q < kStageBatch; ++q) {
+                    const int i = i0 + 256 * q;
+                    const int j = i / I4, c4 = i - j * I4;
+                    v[q] = i < n4 ? *reinterpret_cast<const float4*>(hsrc + (size_t)j * hstride + 4 * c4)
+                                  : float4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+#pragma unroll
+                for (int q = 0; q < kStageBatch; ++q) {
+                    const int i = i0 + 256 * q;
+                    if (i < n4) {
+                        const uint32_t h0 = f32_to_bf16_rne(v[q].x), h1 = f32_to_bf16_rne(v[q].y);
+                        const uint32_t h2 = f32_to_bf16_rne(v[q].z), h3 = f32_to_bf16_rne(v[q].w);
+                        const uint32_t l0 = f32_to_bf16_rne(v[q].x - __uint_as_float(h0 << 16));
+                        const uint32_t l1 = f32_to_bf16_rne(v[q].y - __uint_as_float(h1 << 16));
+                        const uint32_t l2 = f32_to_bf16_rne(v[q].z - __uint_as_float(h2 << 16));
+                        const uint32_t l3 = f32_to_bf16_rne(v[q].w - __uint_as_float(h3 << 16));
+                        reinterpret_cast<uint2*>(s_hh)[i] = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
+                        reinterpret_cast<uint2*>(s_hl)[i] = uint2{l0 | (l1 << 16), l2 | (l3 << 16)};
+                    }
+                }
             }
         }
         __syncthreads();
