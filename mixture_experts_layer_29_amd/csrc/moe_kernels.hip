@@ -702,40 +702,68 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
     const u32x4 zero = u32x4{0, 0, 0, 0};
 
     uint32_t* s_hl = s_hh + (size_t)T * I / 2;
-    // h rows to LDS as bf16 hi + lo pairs (when they fit) and the tokens'
-    // output row offsets; called once the band's first weights are requested.
-    // A thread requests kStageBatch float4 of h at a time: a many-token tile
-    // stages up to 16 per thread, and one at a time would be as many L2 round
-    // trips in a row.
-    auto stage = [&]() {
-        if (tid < T) s_dsto[tid] = (routed ? a.perm[off_r + tid] : sblk * B + tid) * H;
-        if (h_lds) {
-            constexpr int kStageBatch = 2;
-            const int I4 = I / 4, n4 = T * I4;
-            for (int i0 = tid; i0 < n4; i0 += 256 * kStageBatch) {
-                float4 v[kStageBatch];
+    // h rows go to LDS as bf16 hi + lo pairs (when they fit).  A thread's
+    // first float4 of h (one on GEMV tiles, two on MFMA tiles: all of h for up
+    // to 4 / 8 tokens at I = 256) are requested before the weights: loads
+    // complete in issue order, so they arrive first and are staged while the
+    // weights stream.  The rest of a
+    // larger tile's h is requested after the weights, two float4 at a time.
+    // (More than two ahead of the MFMA tile's weights exceeds its registers.)
+    constexpr int kHFirst = 2;
+    constexpr std::integral_constant<int, 1> kGemvFirst{};
+    constexpr std::integral_constant<int, kHFirst> kMfmaFirst{};
+    const int I4 = I / 4, n4 = h_lds ? T * I4 : 0;
+    float4 hv[kHFirst];
+    int pv = 0;
+    auto h_issue = [&](auto nfirst) {
+        constexpr int NF = decltype(nfirst)::value;
+        // unconditional loads (clamped indices; the extra values are unused)
 #pragma unroll
-                for (int q = 0; q < kStageBatch; ++q) {
-                    const int i = i0 + 256 * q;
-                    const int j = i / I4, c4 = i - j * I4;
-                    v[q] = i < n4 ? *reinterpret_cast<const float4*>(hsrc + (size_t)j * hstride + 4 * c4)
-                                  : float4{0.0f, 0.0f, 0.0f, 0.0f};
-                }
+        for (int q = 0; q < NF; ++q) {
+            const int i = max(min(tid + 256 * q, n4 - 1), 0);
+            const int j = i / I4, c4 = i - j * I4;
+            hv[q] = *reinterpret_cast<const float4*>(hsrc + (size_t)j * hstride + 4 * c4);
+        }
+    };
+    // the tokens' pair ids, requested after the weights (at the join of the
+    // GEMV and MFMA paths the compiler waits for every load in flight)
+    auto perm_issue = [&]() {
+        const int pl = a.perm[routed ? off_r + min(tid, T - 1) : 0];
+        pv = routed ? pl : sblk * B + tid;
+    };
+    auto put = [&](int i, const float4 v) {
+        const uint32_t h0 = f32_to_bf16_rne(v.x), h1 = f32_to_bf16_rne(v.y);
+        const uint32_t h2 = f32_to_bf16_rne(v.z), h3 = f32_to_bf16_rne(v.w);
+        const uint32_t l0 = f32_to_bf16_rne(v.x - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16_rne(v.y - __uint_as_float(h1 << 16));
+        const uint32_t l2 = f32_to_bf16_rne(v.z - __uint_as_float(h2 << 16));
+        const uint32_t l3 = f32_to_bf16_rne(v.w - __uint_as_float(h3 << 16));
+        reinterpret_cast<uint2*>(s_hh)[i] = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
+        reinterpret_cast<uint2*>(s_hl)[i] = uint2{l0 | (l1 << 16), l2 | (l3 << 16)};
+    };
+    // called once the band's weights are requested
+    auto stage = [&](auto nfirst) {
+        constexpr int NF = decltype(nfirst)::value;
 #pragma unroll
-                for (int q = 0; q < kStageBatch; ++q) {
-                    const int i = i0 + 256 * q;
-                    if (i < n4) {
-                        const uint32_t h0 = f32_to_bf16_rne(v[q].x), h1 = f32_to_bf16_rne(v[q].y);
-                        const uint32_t h2 = f32_to_bf16_rne(v[q].z), h3 = f32_to_bf16_rne(v[q].w);
-                        const uint32_t l0 = f32_to_bf16_rne(v[q].x - __uint_as_float(h0 << 16));
-                        const uint32_t l1 = f32_to_bf16_rne(v[q].y - __uint_as_float(h1 << 16));
-                        const uint32_t l2 = f32_to_bf16_rne(v[q].z - __uint_as_float(h2 << 16));
-                        const uint32_t l3 = f32_to_bf16_rne(v[q].w - __uint_as_float(h3 << 16));
-                        reinterpret_cast<uint2*>(s_hh)[i] = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
-                        reinterpret_cast<uint2*>(s_hl)[i] = uint2{l0 | (l1 << 16), l2 | (l3 << 16)};
-                    }
-                }
+        for (int q = 0; q < NF; ++q) {
+            const int i = tid + 256 * q;
+            if (i < n4) put(i, hv[q]);
+        }
+        // keep the pair ids' store (which waits for every load) after h's
+        __builtin_amdgcn_sched_barrier(0);
+        if (tid < T) s_dsto[tid] = pv * H;
+        for (int i0 = tid + 256 * NF; i0 < n4; i0 += 512) {
+            float4 v[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int i = i0 + 256 * q;
+                const int j = i / I4, c4 = i - j * I4;
+                v[q] = i < n4 ? *reinterpret_cast<const float4*>(hsrc + (size_t)j * hstride + 4 * c4)
+                              : float4{0.0f, 0.0f, 0.0f, 0.0f};
             }
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                if (i0 + 256 * q < n4) put(i0 + 256 * q, v[q]);
         }
         __syncthreads();
     };
@@ -747,19 +775,23 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
         auto load = [&](int q0, u32x4 (&w)[QB][NQ]) {
 #pragma unroll
             for (int q = 0; q < QB; ++q) {
-                const int row = band + (q0 + q) * RW + rw;
-                const bool ok = band_ok && q0 + q < P;
+                // a band past H (H not a multiple of 256) reads band 0's rows
+                // and stores nothing: no load is conditional, so the waits for
+                // h and for the first batch count the loads issued after them
+                const int row = (band_ok ? band : 0) + (q0 + q) * RW + rw;
 #pragma unroll
                 for (int u = 0; u < NQ; ++u)
-                    w[q][u] = ok ? ld16_stream(W + (size_t)row * ld + 8 * (c + LPR * u)) : zero;
+                    w[q][u] = q0 + q < P ? ld16_stream(W + (size_t)row * ld + 8 * (c + LPR * u)) : zero;
             }
         };
         // two register buffers; the batch loop is unrolled, so they alternate
         // without copies and each batch's loads are waited for only when used
         u32x4 wbuf[2][QB][NQ];
+        h_issue(kGemvFirst);
         load(0, wbuf[0]);
         if (QB < P) load(QB, wbuf[1]);
-        stage();
+        perm_issue();
+        stage(kGemvFirst);
 #pragma unroll
         for (int q0 = 0; q0 < P; q0 += QB) {
             u32x4 (&wa)[QB][NQ] = wbuf[(q0 / QB) & 1];
@@ -787,7 +819,7 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
     } else {
         const int tl = lane & 15, kq = lane >> 4;
         const int NT = (T + 15) >> 4;
-        const uint16_t* arow = W + (size_t)(band + tl) * ld + 8 * kq;  // group g: + 16 g rows
+        const uint16_t* arow = W + (size_t)((band_ok ? band : 0) + tl) * ld + 8 * kq;  // group g: + 16 g rows
         const float* hrow[4];
         bool hok[4];
 #pragma unroll
@@ -802,14 +834,15 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) acc[g][tt] = f32x4{0, 0, 0, 0};
         constexpr int NSC = (LPR * NQ / 4) < 8 ? LPR * NQ / 4 : 8;  // 32-column steps per chunk (I / 32, at most 8)
-        for (int c0 = 0; c0 < I; c0 += 32 * NSC) {
-            u32x4 A[NSC][4];
+        u32x4 A[NSC][4];
+        auto load_a = [&](int c0) {
 #pragma unroll
             for (int st = 0; st < NSC; ++st)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    A[st][g] = band_ok ? ld16_stream(arow + (size_t)16 * g * ld + c0 + 32 * st) : zero;
-            if (c0 == 0) stage();
+                    A[st][g] = ld16_stream(arow + (size_t)16 * g * ld + c0 + 32 * st);
+        };
+        auto chunk = [&](int c0) {
 #pragma unroll
             for (int st = 0; st < NSC; ++st) {
                 const int col = c0 + 32 * st;
@@ -839,6 +872,18 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
                     }
                 }
             }
+        };
+        // the first chunk in straight-line code: h is requested, then the
+        // weights, then h is staged (inside a loop the compiler hoisted the
+        // staging's conversion, and its wait for h, above the weight requests)
+        h_issue(kMfmaFirst);
+        load_a(0);
+        perm_issue();
+        stage(kMfmaFirst);
+        chunk(0);
+        for (int c0 = 32 * NSC; c0 < I; c0 += 32 * NSC) {
+            load_a(c0);
+            chunk(c0);
         }
         // D layout: lane holds rows 4*(lane/16)+r of the group, column (token) lane%16
         if (band_ok) {
