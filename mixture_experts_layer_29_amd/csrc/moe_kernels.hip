@@ -796,20 +796,25 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
         for (int q0 = 0; q0 < P; q0 += QB) {
             u32x4 (&wa)[QB][NQ] = wbuf[(q0 / QB) & 1];
             if (band_ok) {
+                // token-outer: a lane reads its h units of token j from LDS
+                // once per batch of QB rows (row-outer re-read them per row)
+                for (int j = 0; j < T; ++j) {
+                    u32x4 hh[NQ], hl[NQ];
 #pragma unroll
-                for (int q = 0; q < QB; ++q) {
-                    if (q0 + q < P) {
-                        const int row = band + (q0 + q) * RW + rw;
-                        for (int j = 0; j < T; ++j) {
+                    for (int u = 0; u < NQ; ++u) {
+                        const size_t pe = ((size_t)j * I + 8 * (c + LPR * u)) / 2;  // pair index
+                        hh[u] = *reinterpret_cast<const u32x4*>(s_hh + pe);
+                        hl[u] = *reinterpret_cast<const u32x4*>(s_hl + pe);
+                    }
+                    float* drow = dst + s_dsto[j] + band + rw;
+#pragma unroll
+                    for (int q = 0; q < QB; ++q) {
+                        if (q0 + q < P) {
                             float acc = 0.0f;
 #pragma unroll
-                            for (int u = 0; u < NQ; ++u) {
-                                const size_t pe = ((size_t)j * I + 8 * (c + LPR * u)) / 2;  // pair index
-                                acc = dot8_hilo(wa[q][u], *reinterpret_cast<const u32x4*>(s_hh + pe),
-                                                *reinterpret_cast<const u32x4*>(s_hl + pe), acc);
-                            }
+                            for (int u = 0; u < NQ; ++u) acc = dot8_hilo(wa[q][u], hh[u], hl[u], acc);
                             acc = group_sum<LPR>(acc);
-                            if (c == LPR - 1) dst[s_dsto[j] + row] = acc;
+                            if (c == LPR - 1) drow[(q0 + q) * RW] = acc;
                         }
                     }
                 }
