@@ -1101,8 +1101,12 @@ KernelPick pick_down(const DownArgs& a) {
     const int ur = a.I / 8;
     const bool hl = a.h_in_lds != 0;
     const void* f;
-#define MOE_DN(LPR, NQ, RP) \
-    f = hl ? MOE_FN((down_combine_kernel<LPR, NQ, RP, true>)) : MOE_FN((down_combine_kernel<LPR, NQ, RP, false>));
+    int rows;  // output rows per workgroup of the chosen instantiation
+#define MOE_DN(LPR, NQ, RP)                                                                                     \
+    {                                                                                                            \
+        f = hl ? MOE_FN((down_combine_kernel<LPR, NQ, RP, true>)) : MOE_FN((down_combine_kernel<LPR, NQ, RP, false>)); \
+        rows = DownShape<LPR, NQ, RP>::R;                                                                        \
+    }
     if (ur == 8) MOE_DN(8, 1, 1)
     else if (ur == 16) MOE_DN(16, 1, 1)
     else if (ur == 32) MOE_DN(32, 1, 2)
@@ -1111,7 +1115,10 @@ KernelPick pick_down(const DownArgs& a) {
             case 1: MOE_DN(64, 1, 2) break;
             case 2: MOE_DN(64, 2, 2) break;
             case 3: MOE_DN(64, 3, 2) break;
-            case 4: MOE_DN(64, 4, 2) break;
+            // I = 2048 (the unsharded shape at batch 1-2): 16-row workgroups,
+            // 448 at H = 7168, all resident at once; 8-row ones (896) ran a
+            // second, partial generation: 60.8 -> 50.5 us at batch 1
+            case 4: MOE_DN(64, 4, 4) break;
             case 5: MOE_DN(64, 5, 1) break;
             case 6: MOE_DN(64, 6, 1) break;
             case 7: MOE_DN(64, 7, 1) break;
@@ -1120,7 +1127,7 @@ KernelPick pick_down(const DownArgs& a) {
     }
 #undef MOE_DN
     const size_t lds = hl ? down_h_lds_bytes(a.B, a.k, a.I, a.s2 ? a.Is : 0) : (size_t)kDownHStage;
-    return {f, dim3(a.H / down_rows_per_block(a.I)), dim3(256), lds};
+    return {f, dim3(a.H / rows), dim3(256), lds};
 }
 
 // Output-stationary down for batch <= 4, or a null func when the shape has no
