@@ -397,6 +397,79 @@ __global__ __launch_bounds__(256) void gateup_select_kernel(SelGateUpArgs sa) {
     // the routed tiles, grid-strided: the grid is at most what the device
     // holds at once, so each workgroup selects once for all its tiles
     const int ntiles = uni(s_nact) * g.tiles_per_expert;
+    const int gunits = g.H >> 3;
+    if (((gunits + 63) >> 6) <= kMaxGemvUnits) {
+        // software-pipelined: every token's x row is staged once, behind the
+        // first tile's weight requests, and a tile's successor is requested
+        // as soon as the tile's rows are used (no restaging, no barrier and
+        // no h store between a workgroup's tiles)
+        if (b >= ntiles) return;
+        const int tpe = g.tiles_per_expert, H = g.H, G = gridDim.x;
+        u32x4 wg[kMaxGemvUnits], wu[kMaxGemvUnits];
+        auto issue = [&](int tile) {
+            const int entry = tile / tpe;
+            const int i = (tile - entry * tpe) * kPairsPerGemvTile + wave;
+            const uint16_t* gr = g.w + (size_t)uni(s_act_e[entry]) * g.expert_stride + (size_t)i * H;
+            const uint16_t* ur = gr + (size_t)g.n * H;
+#pragma unroll
+            for (int q = 0; q < kMaxGemvUnits; ++q) {
+                const int uu = q * 64 + lane;
+                const bool ok = uu < gunits;
+                wg[q] = ok ? ld16_stream(gr + uu * 8) : zero;
+                wu[q] = ok ? ld16_stream(ur + uu * 8) : zero;
+            }
+        };
+        issue(b);
+        const int nx = a.B * gunits;  // x is [B][H]: unit idx of token idx / units
+        for (int i0 = tid; i0 < nx; i0 += 256 * 8) {
+            u32x4 xr[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) xr[q] = ld16(g.x + (size_t)min(i0 + 256 * q, nx - 1) * 8);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (i0 + 256 * q < nx) st16(s_x + (size_t)(i0 + 256 * q) * 8, xr[q]);
+        }
+        __syncthreads();
+        for (int tile = b; tile < ntiles; tile += G) {
+            const int entry = tile / tpe;
+            const int i = (tile - entry * tpe) * kPairsPerGemvTile + wave;
+            const int off = uni(s_act_off[entry]);
+            int T = uni(s_act_off[entry + 1]) - off;
+            if (T > TB) {  // an expert holds at most one pair per token, so T <= B <= TB
+                if (tid == 0 && i < kPairsPerGemvTile) atomicOr(&g.meta[M_ERR], ERR_TILE);
+                T = 0;
+            }
+            int tk[TB];
+#pragma unroll
+            for (int j = 0; j < TB; ++j) tk[j] = j < T ? uni(s_tok[off + j]) : 0;
+            float ag[TB], au[TB];
+#pragma unroll
+            for (int j = 0; j < TB; ++j) { ag[j] = 0.0f; au[j] = 0.0f; }
+#pragma unroll
+            for (int q = 0; q < kMaxGemvUnits; ++q) {
+                const int uu = q * 64 + lane;
+                if (uu < gunits) {
+#pragma unroll
+                    for (int j = 0; j < TB; ++j) {
+                        if (j < T) {
+                            const u32x4 xv = ld16(s_x + (size_t)tk[j] * H + uu * 8);
+                            ag[j] = dot8(wg[q], xv, ag[j]);
+                            au[j] = dot8(wu[q], xv, au[j]);
+                        }
+                    }
+                }
+            }
+            if (tile + G < ntiles) issue(tile + G);  // the rows are used: the next tile's go out
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                if (j < T) {
+                    const float gs = wave_sum(ag[j]), us = wave_sum(au[j]);
+                    if (lane == 0) st_dev(g.h + (size_t)(off + j) * g.n + i, silu_f(gs) * us);
+                }
+            }
+        }
+        return;
+    }
     for (int tile = b; tile < ntiles; tile += gridDim.x) {
         const int entry = tile / g.tiles_per_expert, local = tile % g.tiles_per_expert;
         const int e = uni(s_act_e[entry]), off = uni(s_act_off[entry]);
