@@ -64,9 +64,9 @@ constexpr int kTopkOneGroupMaxBatch = 8;     // the top-k launch selects in one 
 constexpr size_t kSelectGateupMaxTiles = 512;  // gate/up workgroups of one generation (2 per CU x 256 CUs)
 constexpr size_t kSmallRouterLds = 56 * 1024;
 
-constexpr size_t kLayerLds = 56 * 1024;
+constexpr size_t kLayerLds = 56 * 1024;  // dynamic LDS of the single launch: x staging, then h rows
 constexpr size_t kDownHLds = 48 * 1024;   // output-stationary down: h fully staged in LDS up to this
-constexpr int kDownOsMaxBatch = 4;        // output-stationary down up to this batch, expert-major above  // dynamic LDS of the single launch: x staging, then h rows
+constexpr int kDownOsMaxBatch = 4;        // output-stationary down up to this batch, expert-major above
 
 enum Slot { S_FRONT = 0, S_TOPK = 1, S_GATEUP = 2, S_SHARED = 3, S_DOWN = 4, S_LAYER = 5, S_COMBINE = 6,
             S_EXPERTS = 7, S_COUNT = 8 };
