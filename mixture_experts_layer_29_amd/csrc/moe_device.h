@@ -592,6 +592,9 @@ __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float
 #pragma unroll
                 for (int m = 0; m < NS; ++m) tmp[qq][m] = row[q * qs + min(m * 64 + lane, E - 1)];
             }
+            // keep the adds below every load of the round: interleaved by the
+            // scheduler, they made the round several dependent round trips
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int qq = 0; qq < QC; ++qq)
 #pragma unroll
@@ -625,9 +628,11 @@ __device__ __forceinline__ void select_tokens(const RouterArgs& a, int t0, float
         int my_e;
         float my_z;
         topk_wave<NS>(v, E, k, lane, my_e, my_z);
-        // a full softmax reads the token's logits back: from_acc rows are in a.z (this
-        // wave's stores, complete after the wait)
-        if (from_acc) __builtin_amdgcn_s_waitcnt(0);
+        // a full softmax (no renormalisation) reads the token's logits back:
+        // from_acc rows are in a.z (this wave's stores, complete after the
+        // wait).  Every other weight form needs only the selection, and
+        // skips the wait for the stores' write-through.
+        if (from_acc && a.score_fn == 0 && !a.renormalize) __builtin_amdgcn_s_waitcnt(0);
         route_one(a, t, lane, from_acc ? zo : row, my_e, my_z, __shfl(my_z, 0, 64), s_pair_e, to_global);
     }
     __syncthreads();
