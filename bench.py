@@ -60,8 +60,8 @@ METRIC = "MoE decode layer µs & tokens/s at batch 1/16/64; achieved HBM GB/s vs
 B1_TRAFFIC = {"kernels": {"front": (6360.7, 32.0), "experts": (45048.4, 112.2)},
               "fetch_scale": 2.0, "write_scale": 1.0,
               "sources": {"moe_fused.hip": "63cc114628b5cd87c0444d2f05fc0923af09f53c",
-                          "moe_kernels.hip": "a61ca190380da6de7fae4dda450052097ce0e587",
-                          "moe_device.h": "5fd7e729eceb6821231f6886d565e5cec0fab58b",
+                          "moe_kernels.hip": "49c9948ba3e0e64240815476aaee3820713c3693",
+                          "moe_device.h": "523d680edb4b8081205135604419b051734b918e",
                           "moe_args.h": "7395a498098c31441908d3175290314c83579203"}}
 
 DEFAULT_LINES = ("tp8_b1_prefetch,tp8_b2,tp8_b4,tp8_b8,tp8_b16,tp8_b64,unit_b8,unit_b16,zipf_b64,spec_b8,spec_b64,"
