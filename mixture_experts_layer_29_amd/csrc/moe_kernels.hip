@@ -779,9 +779,9 @@ __global__ __launch_bounds__(256, 2) void down_x_kernel(DownXArgs a) {
     // first float4 of h (one on GEMV tiles, two on MFMA tiles: all of h for up
     // to 4 / 8 tokens at I = 256) are requested before the weights: loads
     // complete in issue order, so they arrive first and are staged while the
-    // weights stream.  The rest of a
-    // larger tile's h is requested after the weights, two float4 at a time.
-    // (More than two ahead of the MFMA tile's weights exceeds its registers.)
+    // weights stream.  The rest of a larger tile's h is requested after the
+    // weights, two float4 at a time.  (More than two ahead of the MFMA tile's
+    // weights exceeds its registers.)
     constexpr int kHFirst = 2;
     constexpr std::integral_constant<int, 1> kGemvFirst{};
     constexpr std::integral_constant<int, kHFirst> kMfmaFirst{};
