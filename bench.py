@@ -60,7 +60,7 @@ METRIC = "MoE decode layer µs & tokens/s at batch 1/16/64; achieved HBM GB/s vs
 B1_TRAFFIC = {"kernels": {"front": (6360.7, 32.0), "experts": (45048.4, 112.2)},
               "fetch_scale": 2.0, "write_scale": 1.0,
               "sources": {"moe_fused.hip": "63cc114628b5cd87c0444d2f05fc0923af09f53c",
-                          "moe_kernels.hip": "49c9948ba3e0e64240815476aaee3820713c3693",
+                          "moe_kernels.hip": "2df34530ae8683fc4340f7e22dd489f802067ade",
                           "moe_device.h": "523d680edb4b8081205135604419b051734b918e",
                           "moe_args.h": "7395a498098c31441908d3175290314c83579203"}}
 
