@@ -79,8 +79,9 @@ typedef struct moe_decode_config {
     const float* router_bias;/* device fp32 [E] added to the logits, or NULL          */
     int32_t force_variant;   /* moe_variant                                           */
     int32_t mfma_min_tokens; /* SPLIT_K: token count from which an expert uses MFMA
-                                tiles; 0 = library default (5, or less where the
-                                GEMV tiles' activation staging does not fit)         */
+                                tiles; 0 = library default (3 at batch 5-16, else
+                                5, or less where the GEMV tiles' activation
+                                staging does not fit)                                */
     int32_t shared_stream;   /* (the Kimi K3 decode article, Part 1 section 3: the
                                 shared expert on a stream of its own, overlapped
                                 with routing)

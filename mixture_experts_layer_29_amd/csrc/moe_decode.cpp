@@ -58,6 +58,9 @@ moe_status fail(moe_status st, const char* fmt, ...) {
 // one-round GEMV tiles than as MFMA tiles with their atomics and last-arriver
 // epilogue (batch 64, TP8 shard: 352 -> 347 us); capped by the GEMV tiles' LDS.
 constexpr int kDefaultMfmaMin = 5;
+// batch 5-16: experts from 3 tokens on MFMA tiles (measured 1-3 us faster at
+// batch 8 / 16 than from 5; at batch 64 it is not)
+constexpr int kDefaultMfmaMinSmall = 3, kMfmaMinSmallMaxBatch = 16;
 constexpr int kMaxProfiledForwards = 1024;
 constexpr int kSmallRouterMaxBatch = 4;
 constexpr int kTopkOneGroupMaxBatch = 8;     // the top-k launch selects in one workgroup up to this batch
@@ -836,7 +839,9 @@ moe_status moe_decode_plan(const moe_decode_config* cfg, moe_decode_plan_t* out_
     p->variant = c.force_variant != MOE_VARIANT_AUTO ? c.force_variant
                  : (c.batch <= 2 && c.batch <= gemv_cap ? MOE_VARIANT_SMALL_M : MOE_VARIANT_SPLIT_K);
     if (p->variant == MOE_VARIANT_SPLIT_K) {
-        p->mfma_min = c.mfma_min_tokens ? c.mfma_min_tokens : kDefaultMfmaMin;
+        p->mfma_min = c.mfma_min_tokens                                          ? c.mfma_min_tokens
+                      : c.batch > kSmallRouterMaxBatch && c.batch <= kMfmaMinSmallMaxBatch ? kDefaultMfmaMinSmall
+                                                                                           : kDefaultMfmaMin;
         if (p->mfma_min > kMaxBatch + 1) p->mfma_min = kMaxBatch + 1;
         if (p->mfma_min > gemv_cap + 1) p->mfma_min = std::max(1, gemv_cap + 1);
         p->routed_gemv_tb = std::max(1, std::min(c.batch, p->mfma_min - 1));
