@@ -29,7 +29,7 @@ def tp8():
     return DeviceLayer(synthetic.TP8)
 
 
-@pytest.mark.parametrize("B,deterministic", [(1, True), (3, True), (16, False), (64, False)])
+@pytest.mark.parametrize("B,deterministic", [(1, True), (2, True), (3, True), (8, False), (16, False), (64, False)])
 def test_forwards_next_to_a_bandwidth_hog(tp8, B, deterministic):
     shape = shape_of(synthetic.TP8)
     plan = make_plan(tp8, shape, B)
