@@ -526,6 +526,8 @@ def main():
         if name == "tp8_b1":
             continue
         sweep[name] = {k: v for k, v in r.items() if not k.startswith("_") and k != "wl"}
+        if "hbm_GBps" in r and cg:
+            sweep[name]["hbm_frac_of_copy"] = r["hbm_GBps"] / cg
         if name in parity:
             sweep[name]["parity"] = parity[name]
     line = {
@@ -548,7 +550,8 @@ def main():
         "config": {"workload": "TP8-shard MoE decode layer, batch 1", "timing": head["timing"],
                    "hidden": wl.hidden, "n_experts": wl.n_experts, "top_k": wl.top_k, "inter": wl.inter,
                    "shared_inter": wl.shared_inter, "batch": 1, "score": "sigmoid, renormalised",
-                   "layers_rotated": args.layers, "activation_batches_rotated": args.batches},
+                   "layers_rotated": args.layers, "activation_batches_rotated": args.batches,
+                   "seed": wl.seed},
         "layer_us": head["layer_us"],
         "layer_us_per_call": head["layer_us_per_call"],
         "hbm_GBps": head["hbm_GBps"],
@@ -557,6 +560,9 @@ def main():
         "n_kernels": head["n_kernels"],
         "kernel_us": head["kernel_us"],
         "copy_GBps": cg,
+        # the layer's unique-weight rate against the device copy's rate (read +
+        # write bytes per second of a 2 GiB copy), a measured ceiling beside 8 TB/s
+        "hbm_frac_of_copy": head["hbm_GBps"] / cg if cg else None,
         "roofline": {"scope": "whole layer: unique routed + shared expert weight bytes per step / step time",
                      "bound": "hbm", "achieved": head["hbm_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": head["hbm_frac"], "traffic": None if traffic is None else traffic["layer"],
